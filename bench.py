@@ -1,0 +1,230 @@
+"""Throughput of the fused block-wise 8-bit Adam step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama7b]
+
+A step is one qopt_adam8bit_step over the whole parameter set (dequantize the 8-bit
+moments, update m, v and p, requantize m and v block-wise), inputs resident in HBM.
+Default workload: the Llama-shaped 7B parameter set (291 tensors, fp32 master
+weights, bf16 gradients with 0.01 % outliers x1000, uint8 moments + fp32 per-block
+absmax), state warmed by 5 steps before the warm-up.  Prints one JSON line.
+
+roofline.achieved = algorithmic bytes of the timed launches / their time, measured
+with HIP events recorded on the stream the kernels run on (torch's current stream).
+Algorithmic bytes per tensor: n * (read p, g, m code, v code + write p, m code,
+v code) + ceil(n / 2048) * 16 (read and write both block maxima).
+cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_adam8bit_llama7b.json")
+KERNEL_SRC = os.path.join(ROOT, "block_wise_bit_adam8bit_amd", "csrc", "qopt_kernels.hip")
+METRIC = "8-bit Adam params/s per step and % of HBM roofline (bytes/param) at 1 GPU"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(sizes, pbytes, gbytes):
+    total = 0
+    for n in sizes:
+        nb = -(-n // 2048)
+        total += n * (2 * pbytes + gbytes + 4) + nb * 16
+    return total
+
+
+def kernel_source_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def load_traffic(launch_bytes):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def make_workload(name, torch, workloads):
+    """Device tensors of the workload: (tensors, sizes, pdtype, gdtype, label)."""
+    if name == "llama7b":
+        shapes, pdt, gdt, seed = workloads.llama7b_shapes(), torch.float32, torch.bfloat16, 3
+        label = ("llama7b: 291 tensors, 6,738,415,616 params, fp32 params, bf16 grads "
+                 "N(0,1e-3) with 0.01% x1000 outliers, uint8 m/v + fp32 absmax per 2048")
+    elif name == "gpt1p3b":
+        shapes, pdt, gdt, seed = workloads.gpt1p3b_shapes(), torch.float32, torch.bfloat16, 2
+        label = "gpt1p3b: 243 tensors, 1,311,086,592 params, fp32 params, bf16 grads"
+    elif name == "flat20b":
+        shapes, pdt, gdt, seed = [("flat", workloads.FLAT20B_N)], torch.bfloat16, torch.bfloat16, 4
+        label = "flat20b: one flat bf16 buffer of 2e10 params updated in place, bf16 grads"
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    sizes = [n for _, n in shapes]
+    total = sum(sizes)
+    dev = torch.device("cuda", 0)
+    P = torch.empty(total, dtype=pdt, device=dev)
+    G = torch.empty(total, dtype=gdt, device=dev)
+    CM = torch.zeros(total, dtype=torch.uint8, device=dev)
+    CV = torch.zeros(total, dtype=torch.uint8, device=dev)
+    workloads.fill_normal_(P, 0.02, seed)
+    if name == "flat20b":
+        workloads.fill_normal_(G, 5e-4, seed * 1000 + 1)
+        rows, dim = workloads.FLAT20B_EMBED_ROWS, workloads.FLAT20B_EMBED_DIM
+        mask = workloads.sparse_rows_mask(rows, workloads.FLAT20B_ACTIVE_ROWS, seed, dev)
+        G[:rows * dim].view(rows, dim)[~mask] = 0
+    else:
+        workloads.fill_normal_(G, 1e-3, seed * 1000 + 1)
+        if name == "llama7b":
+            workloads.scale_random_entries_(G, 1e-4, 1000.0, seed * 1000 + 1)
+    tensors, off = [], 0
+    for n in sizes:
+        nb = -(-n // 2048)
+        tensors.append((P[off:off + n], G[off:off + n], CM[off:off + n], CV[off:off + n],
+                        torch.zeros(nb, dtype=torch.float32, device=dev),
+                        torch.zeros(nb, dtype=torch.float32, device=dev)))
+        off += n
+    return tensors, sizes, pdt, gdt, label
+
+
+def cpu_baseline(target_seconds=12.0):
+    """The oracle, as it stands, on a sample of the llama7b workload: 2048 blocks
+    (4,194,304 params) of fp32 params and bf16 gradients, stepped repeatedly."""
+    import numpy as np
+    import oracle
+    import workloads
+
+    n = 2048 * 2048
+    rng = np.random.default_rng(3)
+    p = workloads.host_normal(n, 0.02, 31)
+    g = oracle.f32_to_bf16_rne(workloads.host_normal(n, 1e-3, 32))
+    st = [np.zeros(n, np.uint8), np.zeros(n, np.uint8), np.zeros(2048, np.float32),
+          np.zeros(2048, np.float32)]
+    del rng
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        out = oracle.adam8bit_step(p, g, *st, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                                   step=steps + 1, grad_dtype="bf16")
+        p, st = out[0], list(out[1:])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= target_seconds or steps >= 50:
+            break
+    return {"value": n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} oracle steps over 4,194,304 params (2048 blocks) of the "
+                      f"llama7b workload's dtypes (fp32 params, bf16 grads), {el:.1f} s; "
+                      f"numpy element-wise ops run on one core of {os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama7b",
+                    choices=["llama7b", "gpt1p3b", "flat20b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the step needs "
+              "no communication and is measured at one GPU's share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    import block_wise_bit_adam8bit_amd as q
+
+    torch.cuda.set_device(0)
+    log(f"building workload {args.workload}")
+    tensors, sizes, pdt, gdt, label = make_workload(args.workload, torch, workloads)
+    prepared = q.make_tensor_array(tensors)
+    launches = q.qopt_adam8bit_launch_count(tensors, _prepared=prepared)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    pbytes = 4 if pdt == torch.float32 else 2
+    gbytes = 4 if gdt == torch.float32 else 2
+    step_bytes = algorithmic_bytes(sizes, pbytes, gbytes)
+    nparams = sum(sizes)
+
+    step = 0
+
+    def one_step():
+        nonlocal step
+        step += 1
+        q.qopt_adam8bit_step(tensors, step=step, _prepared=prepared, **hp)
+
+    warm_state = 5 if args.workload != "flat20b" else 0
+    log(f"{nparams} params, {launches} launches per step; {warm_state} state-warming steps, "
+        f"{args.warmup} warm-up steps, {args.steps} timed steps")
+    for _ in range(warm_state + args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        one_step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / args.steps
+    log(f"timed: wall {wall:.4f} s, events {ev_ms:.3f} ms")
+
+    avg_launch_s = ev_ms * 1e-3 / (args.steps * launches)
+    launch_bytes = step_bytes / launches
+    achieved = launch_bytes / avg_launch_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(launch_bytes),
+                "kernel": "adam8bit_kernel", "launches_per_step": launches,
+                "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                "algorithmic_bytes_per_launch": int(launch_bytes)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del tensors, prepared
+        torch.cuda.empty_cache()
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline()
+
+    out = {
+        "metric": METRIC,
+        "value": nparams / (ms_per_step * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if pdt == torch.float32 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": label, "params": nparams, "tensors": len(sizes),
+                   "bytes_per_param": round(step_bytes / nparams, 4),
+                   "algorithmic_bytes_per_step": step_bytes, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,21 @@
+"""block_wise_bit_adam8bit_amd: block-wise dynamic-tree 8-bit Adam for MI355X.
+
+The compute lives in libqopt.so (HIP kernels for gfx950 behind the C ABI of
+include/qopt.h); this package is its thin Python binding plus a torch optimizer.
+Importing it loads the library and fails with ImportError if it is not built.
+"""
+
+from ._lib import (  # noqa: F401
+    LIB, LIB_PATH, QOPT_BLOCK, QoptError, status_string,
+    QOPT_OK, QOPT_EINVAL, QOPT_EUNSUPPORTED, QOPT_EALIGN, QOPT_ELAUNCH, QOPT_EINTERNAL,
+    QOPT_CB_SIGNED, QOPT_CB_UNSIGNED, QOPT_F32, QOPT_BF16,
+)
+from .functional import (  # noqa: F401
+    SIGNED, UNSIGNED, nblocks, codebook, codebook_bytes, qopt_codebook_build,
+    qopt_quantize_blockwise, qopt_dequantize_blockwise, qopt_adam8bit_step,
+    qopt_adam8bit_launch_count,
+    make_tensor_array,
+)
+from .optim import Adam8bit  # noqa: F401
+
+__version__ = "0.1.0"

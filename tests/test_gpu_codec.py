@@ -1,0 +1,168 @@
+"""GPU parity of the block-wise quantize / dequantize kernels against the oracle.
+
+Codes and absmax must be bit-exact; dequantized values too (one binary32 multiply
+on both sides).  Sizes span several blocks and ragged tails; the full 2^28-value
+Student-t workload is checked on sampled blocks plus whole-size properties; every
+binary32 in [0, 1] is swept through both codebooks.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+KINDS = [oracle.SIGNED, oracle.UNSIGNED]
+SIZES = [1, 7, 2047, 2048, 2049, 50257, 3 * 2048 + 5, 40 * 2048 + 1234]
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def q():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_wise_bit_adam8bit_amd as q
+    torch.cuda.set_device(0)
+    return q
+
+
+def _check_codec(q, x, kind, xd=None, codes=None, absmax=None):
+    xd = torch.from_numpy(x).cuda() if xd is None else xd
+    c, a = q.qopt_quantize_blockwise(xd, kind, codes=codes, absmax=absmax)
+    y = q.qopt_dequantize_blockwise(c, a, kind)
+    c_ref, a_ref = oracle.quantize_blockwise(x, kind)
+    y_ref = oracle.dequantize_blockwise(c_ref, a_ref, kind)
+    torch.cuda.synchronize()
+    c_got = c.cpu().numpy()
+    bad = np.nonzero(c_got != c_ref)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, first at {bad[:5]}: {c_got[bad[:5]]} vs {c_ref[bad[:5]]}"
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), a_ref.view(np.uint32))
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("n", SIZES)
+def test_codec_matches_oracle(q, kind, n):
+    say(f"codec kind={kind} n={n}")
+    x = workloads.student_t3_host(n, seed=n)
+    _check_codec(q, x, kind)
+    if kind == oracle.UNSIGNED:
+        _check_codec(q, np.abs(x), kind)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_codec_misaligned_views(q, kind):
+    """Views at element offsets that break 16-byte (x) and 4-byte (codes) alignment
+    take the element-wise path and still match."""
+    n = 5 * 2048 + 99
+    x = workloads.student_t3_host(n, seed=5)
+    buf = torch.zeros(n + 3, dtype=torch.float32, device="cuda")
+    buf[1:n + 1] = torch.from_numpy(x).cuda()
+    cbuf = torch.zeros(n + 3, dtype=torch.uint8, device="cuda")
+    say(f"codec misaligned kind={kind}")
+    _check_codec(q, x, kind, xd=buf[1:n + 1], codes=cbuf[3:n + 3])
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_codec_special_blocks(q, kind):
+    """Zero, subnormal, constant, single-outlier, signed-zero and threshold blocks."""
+    B = 2048
+    T = oracle.code_transitions(kind)
+    mags = oracle.magnitudes_f32(kind)
+    blocks = [np.zeros(B, np.float32),
+              np.full(B, 1e-40, np.float32),
+              np.full(B, -3.5, np.float32),
+              np.full(B, 2.0 ** -126, np.float32)]
+    out = np.random.default_rng(1).normal(0, 1e-3, B).astype(np.float32)
+    out[77] = 1e3
+    blocks.append(out)
+    sz = np.zeros(B, np.float32)
+    sz[::2] = -0.0
+    sz[5] = -1e-9
+    sz[6] = 1.0
+    blocks.append(sz)
+    # values on and next to every decision threshold and table value, absmax 1
+    adv = np.concatenate([T, np.nextafter(T, np.float32(0)), np.nextafter(T, np.float32(2)),
+                          mags, (mags[:-1] + mags[1:]) / 2]).astype(np.float32)
+    adv = np.concatenate([[1.0], adv, -adv if kind == oracle.SIGNED else adv]).astype(np.float32)
+    adv = np.resize(adv, (-(-adv.size // B)) * B)
+    adv[::B] = 1.0
+    blocks.append(adv)
+    x = np.concatenate(blocks).astype(np.float32)
+    say(f"codec special blocks kind={kind} n={x.size}")
+    _check_codec(q, x, kind)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_exhaustive_unit_interval(q, kind):
+    """Every binary32 in [0, 1] (and, signed, its negation) is quantized in blocks
+    whose absmax is exactly 1.0, so the kernel encodes the value itself.  The codes
+    of the ordered sweep must step by one exactly at the oracle's transition points
+    (code_transitions, built only from the oracle's nearest rule)."""
+    N = int(np.float32(1.0).view(np.uint32)) + 1           # bit patterns 0 .. 1.0
+    per = 2047
+    nblk = -(-N // per)
+    say(f"exhaustive sweep kind={kind}: {N} values in {nblk} blocks")
+    x = torch.zeros(nblk * 2048, dtype=torch.float32, device="cuda")
+    xv = x.view(nblk, 2048)
+    xv[:, 0] = 1.0
+    body = xv[:, 1:].reshape(-1)
+    body[:N] = torch.arange(0, N, dtype=torch.int32, device="cuda").view(torch.float32)
+    T = oracle.code_transitions(kind)
+    want_pos = T.view(np.uint32).astype(np.int64)          # sweep index == bit pattern
+    nmag = T.size + 1
+    for sign in ([1.0, -1.0] if kind == oracle.SIGNED else [1.0]):
+        if sign < 0:
+            body[:N].neg_()
+        codes, absmax = q.qopt_quantize_blockwise(x, kind)
+        assert bool((absmax == 1.0).all())
+        sc = codes.view(nblk, 2048)[:, 1:].reshape(-1)[:N]
+        mag = (sc & 0x7F) if kind == oracle.SIGNED else sc
+        change = torch.nonzero(mag[1:] != mag[:-1]).flatten() + 1
+        got_pos = change.cpu().numpy()
+        assert np.array_equal(got_pos, want_pos), (got_pos[:5], want_pos[:5])
+        steps = (mag[change].int() - mag[change - 1].int()).cpu().numpy()
+        assert np.all(steps == 1)
+        assert int(mag[0]) == 0 and int(mag[-1]) == nmag - 1
+        if kind == oracle.SIGNED:
+            signs = (sc & 0x80) != 0
+            if sign > 0:
+                assert not bool(signs.any())
+            else:   # every negative value carries the sign bit; -0.0 does not
+                assert not bool(signs[0]) and bool(signs[1:].all())
+        torch.cuda.synchronize()
+    del x, codes, absmax
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_full_size_student_t(q, kind):
+    """2^28 values 0.01 * Student-t(3) (|x| for the unsigned codebook): sampled
+    blocks against the oracle, and every block's absmax against torch.amax."""
+    n = 1 << 28
+    nblk = n // 2048
+    say(f"full-size codec kind={kind} n={n}")
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    workloads.student_t3_(x, seed=1)
+    if kind == oracle.UNSIGNED:
+        x.abs_()
+    codes, absmax = q.qopt_quantize_blockwise(x, kind)
+    y = q.qopt_dequantize_blockwise(codes, absmax, kind)
+    amax = x.view(nblk, 2048).abs().amax(dim=1)
+    assert torch.equal(absmax, amax)
+    sample = workloads.sample_blocks(nblk, 1500, seed=kind)
+    idx = torch.from_numpy(sample).cuda()
+    xs = x.view(nblk, 2048)[idx].cpu().numpy().reshape(-1)
+    cs = codes.view(nblk, 2048)[idx].cpu().numpy().reshape(-1)
+    ys = y.view(nblk, 2048)[idx].cpu().numpy().reshape(-1)
+    c_ref, a_ref = oracle.quantize_blockwise(xs, kind)
+    assert np.array_equal(cs, c_ref)
+    assert np.array_equal(absmax[idx].cpu().numpy(), a_ref)
+    assert np.array_equal(ys.view(np.uint32),
+                          oracle.dequantize_blockwise(c_ref, a_ref, kind).view(np.uint32))
+    del x, codes, absmax, y, amax
+    torch.cuda.empty_cache()
