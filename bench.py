@@ -129,14 +129,69 @@ def cpu_baseline(target_seconds=12.0):
                       f"numpy element-wise ops run on one core of {os.cpu_count()}"}
 
 
+def calibrate_copy(torch, reps):
+    """Plain device copies of a known size: what PMC byte counters read for them
+    scales the counters of the step kernel."""
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "torch copy_", "bytes_read_per_copy": 4 * n,
+                      "bytes_written_per_copy": 4 * n, "copies": reps}), flush=True)
+
+
+def bench_codec(torch, workloads, q, args):
+    """Block-wise quantize and dequantize of 2^28 values 0.01 * Student-t(3)."""
+    n = 1 << 28
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    workloads.student_t3_(x, seed=1)
+    codes = torch.empty(n, dtype=torch.uint8, device="cuda")
+    absmax = torch.empty(n // 2048, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(args.warmup + 1):
+        q.qopt_quantize_blockwise(x, q.SIGNED, codes=codes, absmax=absmax)
+        q.qopt_dequantize_blockwise(codes, absmax, q.SIGNED, out=y)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tq = td = 0.0
+    for _ in range(args.steps):
+        ev[0].record()
+        q.qopt_quantize_blockwise(x, q.SIGNED, codes=codes, absmax=absmax)
+        ev[1].record()
+        q.qopt_dequantize_blockwise(codes, absmax, q.SIGNED, out=y)
+        ev[2].record()
+        torch.cuda.synchronize()
+        tq += ev[0].elapsed_time(ev[1])
+        td += ev[1].elapsed_time(ev[2])
+    tq, td = tq / args.steps, td / args.steps
+    byts = n * 5 + (n // 2048) * 4
+    out = {"metric": "block-wise dynamic-tree quantize + dequantize values/s at 1 GPU",
+           "value": n / ((tq + td) * 1e-3), "unit": "values/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tq + td, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": "codec256m: 2^28 fp32 values 0.01*Student-t(3), signed "
+                                  "codebook, 131,072 blocks of 2048"},
+           "kernels": {"quantize": {"ms": round(tq, 4), "GB/s": round(byts / tq / 1e6, 1),
+                                    "frac": round(byts / tq / 1e6 / HBM_PEAK_GBS, 4)},
+                       "dequantize": {"ms": round(td, 4), "GB/s": round(byts / td / 1e6, 1),
+                                      "frac": round(byts / td / 1e6 / HBM_PEAK_GBS, 4)}}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "gpt1p3b", "flat20b"])
+                    choices=["llama7b", "gpt1p3b", "flat20b", "codec256m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run torch copies of 4 GiB (for scaling PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the step needs "
@@ -148,6 +203,10 @@ def main():
     import block_wise_bit_adam8bit_amd as q
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        return calibrate_copy(torch, args.steps)
+    if args.workload == "codec256m":
+        return bench_codec(torch, workloads, q, args)
     log(f"building workload {args.workload}")
     tensors, sizes, pdt, gdt, label = make_workload(args.workload, torch, workloads)
     prepared = q.make_tensor_array(tensors)

@@ -35,6 +35,13 @@ constexpr int kWaves = 4;                       // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kSlices = QOPT_BLOCK / (kWave * 4);  // 8 slices of 4 elements per lane
 constexpr int kMaxTensors = 48;                 // tensors per launch (kernarg budget)
+// The step keeps a block's 32 m and v values per lane plus the prefetched inputs
+// of the next block in registers: about 240 VGPRs, so 2 waves per SIMD.  Asking
+// for 3 makes the compiler spill to scratch, which measured slower.
+#ifndef QOPT_STEP_WAVES_PER_SIMD
+#define QOPT_STEP_WAVES_PER_SIMD 2
+#endif
+constexpr int kStepWavesPerSimd = QOPT_STEP_WAVES_PER_SIMD;
 constexpr int kRows = static_cast<int>(sizeof(qopt_codebook) / 16);
 static_assert(kSlices * kWave * 4 == QOPT_BLOCK, "block layout");
 
@@ -65,6 +72,7 @@ __device__ __forceinline__ void st_stream(T* p, T v) {
 
 // ------------------------------------------------------------------ helpers
 
+
 __device__ __forceinline__ void stage_codebook(qopt_codebook* dst, const qopt_codebook* src) {
   const uint4* s = reinterpret_cast<const uint4*>(src);
   uint4* d = reinterpret_cast<uint4*>(dst);
@@ -88,26 +96,31 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
 // Per-codebook encoder parameters kept in registers for the whole kernel.
 struct Encoder {
   const qopt_codebook* cb;  // LDS copy
-  int32_t key0;
-  int32_t last_bucket;
+  float a_floor;            // the binary32 whose key is key0
+  uint32_t key0;
+  uint32_t last_bucket;
 };
 
 __device__ __forceinline__ Encoder make_encoder(const qopt_codebook* lds_cb) {
   Encoder e;
   e.cb = lds_cb;
-  e.key0 = static_cast<int32_t>(lds_cb->key0);
+  e.key0 = lds_cb->key0;
+  e.a_floor = __uint_as_float(e.key0 << 15);
   uint32_t nb = lds_cb->nbuckets;
   nb = nb < 1u ? 1u : (nb > QOPT_MAX_BUCKETS ? QOPT_MAX_BUCKETS : nb);
-  e.last_bucket = static_cast<int32_t>(nb) - 1;
+  e.last_bucket = nb - 1;
   return e;
 }
 
 // Magnitude index of a >= 0: bucket start index, plus one if a reaches the single
-// threshold that may lie inside the bucket.  Indexes stay inside the tables for any
-// table contents (bucket bytes <= 255, thresh has >= 257 entries).
+// threshold that may lie inside the bucket.  Values below bucket 0 (and NaN) are
+// raised to its start, values above the last bucket are clamped to it, so every
+// index stays inside the tables for any table contents (bucket bytes <= 255,
+// thresh has >= 257 entries).
 __device__ __forceinline__ uint32_t encode_mag(const Encoder& e, float a) {
-  int32_t i = static_cast<int32_t>(__float_as_uint(a) >> 15) - e.key0;
-  i = i < 0 ? 0 : (i > e.last_bucket ? e.last_bucket : i);
+  const float ac = fmaxf(a, e.a_floor);
+  uint32_t i = (__float_as_uint(ac) >> 15) - e.key0;
+  i = i < e.last_bucket ? i : e.last_bucket;
   const uint32_t b = e.cb->bucket[i];
   return b + (a >= e.cb->thresh[b + 1] ? 1u : 0u);
 }
@@ -272,41 +285,41 @@ struct StepChunk {
   uint64_t vector_ok;                    // bit i: piece i may use the vector path
 };
 
-template <typename PT> struct ParamIO;
+// Element types as they sit in memory: fp32, or bf16 bit patterns (uint16_t).
+// Four consecutive elements are one vector access: 16 bytes of fp32, 8 of bf16.
+template <typename T> struct Vec4T;
+template <> struct Vec4T<float> { typedef f32x4 type; };
+template <> struct Vec4T<uint16_t> { typedef u32x2 type; };
 
-template <> struct ParamIO<float> {
-  __device__ static void load4(const void* p, int64_t base, int idx, float out[4]) {
-    const f32x4 v = ld_stream(reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + base) + idx);
-    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
-  }
-  __device__ static void store4(void* p, int64_t base, int idx, const float in[4]) {
-    f32x4 v;
-    v.x = in[0]; v.y = in[1]; v.z = in[2]; v.w = in[3];
-    st_stream(reinterpret_cast<f32x4*>(static_cast<float*>(p) + base) + idx, v);
-  }
-  __device__ static float load1(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
-  __device__ static void store1(void* p, int64_t i, float x) { static_cast<float*>(p)[i] = x; }
-};
+__device__ __forceinline__ void unpack4(const f32x4& v, float o[4]) {
+  o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+}
+__device__ __forceinline__ void unpack4(const u32x2& v, float o[4]) {
+  o[0] = bf16_to_f32(v.x & 0xFFFFu); o[1] = bf16_to_f32(v.x >> 16);
+  o[2] = bf16_to_f32(v.y & 0xFFFFu); o[3] = bf16_to_f32(v.y >> 16);
+}
+__device__ __forceinline__ void pack4(const float in[4], f32x4& v) {
+  v.x = in[0]; v.y = in[1]; v.z = in[2]; v.w = in[3];
+}
+__device__ __forceinline__ void pack4(const float in[4], u32x2& v) {
+  v.x = f32_to_bf16_rne(in[0]) | (f32_to_bf16_rne(in[1]) << 16);
+  v.y = f32_to_bf16_rne(in[2]) | (f32_to_bf16_rne(in[3]) << 16);
+}
 
-template <> struct ParamIO<uint16_t> {  // bf16 bit patterns
-  __device__ static void load4(const void* p, int64_t base, int idx, float out[4]) {
-    const u32x2 v = ld_stream(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + base) + idx);
-    out[0] = bf16_to_f32(v.x & 0xFFFFu); out[1] = bf16_to_f32(v.x >> 16);
-    out[2] = bf16_to_f32(v.y & 0xFFFFu); out[3] = bf16_to_f32(v.y >> 16);
-  }
-  __device__ static void store4(void* p, int64_t base, int idx, const float in[4]) {
-    u32x2 v;
-    v.x = f32_to_bf16_rne(in[0]) | (f32_to_bf16_rne(in[1]) << 16);
-    v.y = f32_to_bf16_rne(in[2]) | (f32_to_bf16_rne(in[3]) << 16);
-    st_stream(reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p) + base) + idx, v);
-  }
-  __device__ static float load1(const void* p, int64_t i) {
-    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-  }
-  __device__ static void store1(void* p, int64_t i, float x) {
-    static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16_rne(x));
-  }
-};
+template <typename T> __device__ __forceinline__ float load1(const void* p, int64_t i);
+template <> __device__ __forceinline__ float load1<float>(const void* p, int64_t i) {
+  return static_cast<const float*>(p)[i];
+}
+template <> __device__ __forceinline__ float load1<uint16_t>(const void* p, int64_t i) {
+  return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+template <typename T> __device__ __forceinline__ void store1(void* p, int64_t i, float x);
+template <> __device__ __forceinline__ void store1<float>(void* p, int64_t i, float x) {
+  static_cast<float*>(p)[i] = x;
+}
+template <> __device__ __forceinline__ void store1<uint16_t>(void* p, int64_t i, float x) {
+  static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16_rne(x));
+}
 
 // One element of the update; returns the new parameter, leaves m and v.
 __device__ __forceinline__ float adam_element(const AdamScalars& k, float p, float g, float m_prev,
@@ -318,92 +331,171 @@ __device__ __forceinline__ float adam_element(const AdamScalars& k, float p, flo
   return p - (k.step_size * u);
 }
 
-template <typename PT, typename GT, bool kVector>
-__device__ __forceinline__ void adam_block(const AdamScalars& k, const qopt_codebook& cbm,
-                                           const qopt_codebook& cbv, const Encoder& em,
-                                           const Encoder& ev, void* param, const void* grad,
-                                           uint8_t* cm, uint8_t* cv, float* am, float* av,
-                                           int64_t base, int len, int lane) {
-  const float Am = *am;
-  const float Av = *av;
-  float m[kSlices][4], v[kSlices][4];
-  float mmax = 0.0f, vmax = 0.0f;
+// Where one block lives, resolved from the launch's piece table (wave-uniform).
+struct BlockRef {
+  void* param;
+  const void* grad;
+  uint8_t* cm;
+  uint8_t* cv;
+  float* am;
+  float* av;
+  int64_t base;  // first element of the block within its tensor
+  int len;       // elements in the block (2048 except a tensor's last block)
+  bool vec;      // full block of a tensor whose pointers allow vector accesses
+};
 
+__device__ __forceinline__ BlockRef resolve(const StepChunk& c, uint32_t blk) {
+  uint32_t lo = 0, hi = c.npieces;  // last piece t with block_start[t] <= blk
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) / 2;
+    if (c.block_start[mid] <= blk) lo = mid; else hi = mid;
+  }
+  const uint32_t t = lo;
+  const uint32_t lb = c.block_lo[t] + (blk - c.block_start[t]);
+  BlockRef r;
+  r.param = c.param[t];
+  r.grad = c.grad[t];
+  r.cm = c.m_codes[t];
+  r.cv = c.v_codes[t];
+  r.am = c.m_absmax[t] + lb;
+  r.av = c.v_absmax[t] + lb;
+  r.base = static_cast<int64_t>(lb) * QOPT_BLOCK;
+  const int64_t rem = c.n[t] - r.base;
+  r.len = rem < QOPT_BLOCK ? static_cast<int>(rem) : QOPT_BLOCK;
+  r.vec = r.len == QOPT_BLOCK && ((c.vector_ok >> t) & 1u);
+  return r;
+}
+
+// One lane's vector inputs of one full block: slice s holds elements
+// s*256 + 4*lane .. +3.
+template <typename PT, typename GT>
+struct BlockIn {
+  typename Vec4T<PT>::type p[kSlices];
+  typename Vec4T<GT>::type g[kSlices];
+  uint32_t cm[kSlices];
+  uint32_t cv[kSlices];
+  float am, av;
+};
+
+template <typename PT, typename GT>
+__device__ __forceinline__ void load_block(BlockIn<PT, GT>& in, const BlockRef& r, int lane) {
+  typedef typename Vec4T<PT>::type PV;
+  typedef typename Vec4T<GT>::type GV;
+  const PV* p = reinterpret_cast<const PV*>(static_cast<const PT*>(r.param) + r.base);
+  const GV* g = reinterpret_cast<const GV*>(static_cast<const GT*>(r.grad) + r.base);
+  const uint32_t* cm = reinterpret_cast<const uint32_t*>(r.cm + r.base);
+  const uint32_t* cv = reinterpret_cast<const uint32_t*>(r.cv + r.base);
+  in.am = *r.am;
+  in.av = *r.av;
 #pragma unroll
   for (int s = 0; s < kSlices; ++s) {
     const int idx = s * kWave + lane;
-    float p4[4], g4[4];
-    uint32_t wm = 0, wv = 0;
-    if (kVector) {
-      ParamIO<PT>::load4(param, base, idx, p4);
-      ParamIO<GT>::load4(grad, base, idx, g4);
-      wm = ld_stream(reinterpret_cast<const uint32_t*>(cm + base) + idx);
-      wv = ld_stream(reinterpret_cast<const uint32_t*>(cv + base) + idx);
-    } else {
+    in.p[s] = ld_stream(p + idx);
+    in.g[s] = ld_stream(g + idx);
+    in.cm[s] = ld_stream(cm + idx);
+    in.cv[s] = ld_stream(cv + idx);
+  }
+}
+
+// Update of a full block from prefetched vector inputs; stores p, keeps m and v.
+template <typename PT, typename GT>
+__device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_codebook& cbm,
+                                           const qopt_codebook& cbv, const BlockIn<PT, GT>& in,
+                                           const BlockRef& r, int lane, float m[kSlices][4],
+                                           float v[kSlices][4], float& mmax, float& vmax) {
+  typedef typename Vec4T<PT>::type PV;
+  PV* pout = reinterpret_cast<PV*>(static_cast<PT*>(r.param) + r.base);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = s * 256 + lane * 4 + j;
-        const bool in = e < len;
-        p4[j] = in ? ParamIO<PT>::load1(param, base + e) : 0.0f;
-        g4[j] = in ? ParamIO<GT>::load1(grad, base + e) : 0.0f;
-        wm |= (in ? static_cast<uint32_t>(cm[base + e]) : 0u) << (8 * j);
-        wv |= (in ? static_cast<uint32_t>(cv[base + e]) : 0u) << (8 * j);
-      }
-    }
+  for (int s = 0; s < kSlices; ++s) {
+    float p4[4], g4[4];
+    unpack4(in.p[s], p4);
+    unpack4(in.g[s], g4);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float m_prev = cbm.decode[(wm >> (8 * j)) & 0xFFu] * Am;
-      const float v_prev = cbv.decode[(wv >> (8 * j)) & 0xFFu] * Av;
+      const float m_prev = cbm.decode[(in.cm[s] >> (8 * j)) & 0xFFu] * in.am;
+      const float v_prev = cbv.decode[(in.cv[s] >> (8 * j)) & 0xFFu] * in.av;
       p4[j] = adam_element(k, p4[j], g4[j], m_prev, v_prev, m[s][j], v[s][j]);
-      if (!kVector && s * 256 + lane * 4 + j >= len) { m[s][j] = 0.0f; v[s][j] = 0.0f; }
       mmax = fmaxf(mmax, fabsf(m[s][j]));
       vmax = fmaxf(vmax, v[s][j]);
     }
-    if (kVector) {
-      ParamIO<PT>::store4(param, base, idx, p4);
-    } else {
+    PV pv;
+    pack4(p4, pv);
+    st_stream(pout + s * kWave + lane, pv);
+  }
+}
+
+// Update of a short block, or of a tensor without vector alignment: element-wise
+// accesses guarded by the block length; elements past it hold m = v = 0.
+template <typename PT, typename GT>
+__device__ __forceinline__ void update_scalar(const AdamScalars& k, const qopt_codebook& cbm,
+                                              const qopt_codebook& cbv, const BlockRef& r,
+                                              int lane, float m[kSlices][4], float v[kSlices][4],
+                                              float& mmax, float& vmax) {
+  const float Am = *r.am;
+  const float Av = *r.av;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = s * 256 + lane * 4 + j;
-        if (e < len) ParamIO<PT>::store1(param, base + e, p4[j]);
+  for (int s = 0; s < kSlices; ++s)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = s * 256 + lane * 4 + j;
+      m[s][j] = 0.0f;
+      v[s][j] = 0.0f;
+      if (e < r.len) {
+        const int64_t i = r.base + e;
+        const float m_prev = cbm.decode[r.cm[i]] * Am;
+        const float v_prev = cbv.decode[r.cv[i]] * Av;
+        const float p = adam_element(k, load1<PT>(r.param, i), load1<GT>(r.grad, i), m_prev,
+                                     v_prev, m[s][j], v[s][j]);
+        store1<PT>(r.param, i, p);
+        mmax = fmaxf(mmax, fabsf(m[s][j]));
+        vmax = fmaxf(vmax, v[s][j]);
       }
     }
-  }
+}
 
-  const BlockScale sm = block_scale(wave_max(mmax), cbm.sign_mask);
-  const BlockScale sv = block_scale(wave_max(vmax), cbv.sign_mask);
-
+// Block maxima across the wave, then the codes of m and v and the new maxima.
+__device__ __forceinline__ void requantize(const Encoder& em, const Encoder& ev, uint32_t sign_m,
+                                           uint32_t sign_v, const BlockRef& r, int lane,
+                                           const float m[kSlices][4], const float v[kSlices][4],
+                                           float mmax, float vmax) {
+  const BlockScale sm = block_scale(wave_max(mmax), sign_m);
+  const BlockScale sv = block_scale(wave_max(vmax), sign_v);
+  uint32_t* cmo = reinterpret_cast<uint32_t*>(r.cm + r.base);
+  uint32_t* cvo = reinterpret_cast<uint32_t*>(r.cv + r.base);
 #pragma unroll
   for (int s = 0; s < kSlices; ++s) {
-    const int idx = s * kWave + lane;
     uint32_t wm = 0, wv = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       wm |= encode_signed(em, sm, m[s][j]) << (8 * j);
       wv |= encode_signed(ev, sv, v[s][j]) << (8 * j);
     }
-    if (kVector) {
-      st_stream(reinterpret_cast<uint32_t*>(cm + base) + idx, wm);
-      st_stream(reinterpret_cast<uint32_t*>(cv + base) + idx, wv);
-    } else {
+    if (r.vec) {
+      st_stream(cmo + s * kWave + lane, wm);
+      st_stream(cvo + s * kWave + lane, wv);
+      } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = s * 256 + lane * 4 + j;
-        if (e < len) {
-          cm[base + e] = static_cast<uint8_t>(wm >> (8 * j));
-          cv[base + e] = static_cast<uint8_t>(wv >> (8 * j));
+        if (e < r.len) {
+          r.cm[r.base + e] = static_cast<uint8_t>(wm >> (8 * j));
+          r.cv[r.base + e] = static_cast<uint8_t>(wv >> (8 * j));
         }
       }
     }
   }
   if (lane == 0) {
-    *am = sm.absmax;
-    *av = sv.absmax;
+    *r.am = sm.absmax;
+    *r.av = sv.absmax;
   }
 }
 
+// Each wave walks blocks blk, blk + stride, ...  While it requantizes one block,
+// the vector inputs of its next block are already in flight (loaded into the
+// registers the update no longer needs), so memory stays busy through the
+// requantization phase.
 template <typename PT, typename GT>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, kStepWavesPerSimd)
 adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qopt_codebook* cbv_g) {
   __shared__ __align__(16) qopt_codebook cb[2];
   stage_codebook(&cb[0], cbm_g);
@@ -411,30 +503,36 @@ adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qo
   __syncthreads();
   const Encoder em = make_encoder(&cb[0]);
   const Encoder ev = make_encoder(&cb[1]);
+  const uint32_t sign_m = cb[0].sign_mask;
+  const uint32_t sign_v = cb[1].sign_mask;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const uint32_t stride = gridDim.x * kWaves;
   const uint32_t total = c.block_start[c.npieces];
 
-  for (uint32_t blk = blockIdx.x * kWaves + wave; blk < total; blk += stride) {
-    // piece owning this block: last t with block_start[t] <= blk (wave-uniform)
-    uint32_t lo = 0, hi = c.npieces;
-    while (hi - lo > 1) {
-      const uint32_t mid = (lo + hi) / 2;
-      if (c.block_start[mid] <= blk) lo = mid; else hi = mid;
+  uint32_t blk = blockIdx.x * kWaves + wave;
+  if (blk >= total) return;
+  BlockRef cur = resolve(c, blk);
+  BlockIn<PT, GT> in;
+  if (cur.vec) load_block(in, cur, lane);
+  for (;;) {
+    float m[kSlices][4], v[kSlices][4];
+    float mmax = 0.0f, vmax = 0.0f;
+    if (cur.vec)
+      update_vec(k, cb[0], cb[1], in, cur, lane, m, v, mmax, vmax);
+    else
+      update_scalar<PT, GT>(k, cb[0], cb[1], cur, lane, m, v, mmax, vmax);
+    const uint32_t nblk = blk + stride;
+    const bool more = nblk < total;
+    BlockRef nxt = cur;
+    if (more) {
+      nxt = resolve(c, nblk);
+      if (nxt.vec) load_block(in, nxt, lane);
     }
-    const uint32_t t = lo;
-    const uint32_t lb = c.block_lo[t] + (blk - c.block_start[t]);
-    const int64_t base = static_cast<int64_t>(lb) * QOPT_BLOCK;
-    const int64_t rem = c.n[t] - base;
-    const int len = rem < QOPT_BLOCK ? static_cast<int>(rem) : QOPT_BLOCK;
-    if (len == QOPT_BLOCK && ((c.vector_ok >> t) & 1u)) {
-      adam_block<PT, GT, true>(k, cb[0], cb[1], em, ev, c.param[t], c.grad[t], c.m_codes[t],
-                               c.v_codes[t], c.m_absmax[t] + lb, c.v_absmax[t] + lb, base, len, lane);
-    } else {
-      adam_block<PT, GT, false>(k, cb[0], cb[1], em, ev, c.param[t], c.grad[t], c.m_codes[t],
-                                c.v_codes[t], c.m_absmax[t] + lb, c.v_absmax[t] + lb, base, len, lane);
-    }
+    requantize(em, ev, sign_m, sign_v, cur, lane, m, v, mmax, vmax);
+    if (!more) break;
+    blk = nblk;
+    cur = nxt;
   }
 }
 

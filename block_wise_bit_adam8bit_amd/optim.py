@@ -9,12 +9,11 @@ the first step.  Parameters must be contiguous fp32 or bf16 GPU tensors with den
 fp32 or bf16 gradients; the update runs in libqopt's fused kernel.
 """
 
+from collections import defaultdict
+
 import torch
 
 from .functional import make_tensor_array, nblocks, qopt_adam8bit_step
-
-_ABSMAX_KEYS = ("m_absmax", "v_absmax")
-
 
 class Adam8bit(torch.optim.Optimizer):
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8):
@@ -75,16 +74,35 @@ class Adam8bit(torch.optim.Optimizer):
         return loss
 
     def load_state_dict(self, state_dict):
-        # torch casts floating-point state to the parameter's dtype on load; the block
-        # maxima must stay fp32, so they travel as int32 bit patterns through it.
-        sd = dict(state_dict)
-        sd["state"] = {
-            k: {kk: (vv.view(torch.int32) if kk in _ABSMAX_KEYS else vv) for kk, vv in v.items()}
-            for k, v in state_dict["state"].items()
-        }
-        super().load_state_dict(sd)
-        for st in self.state.values():
-            for k in _ABSMAX_KEYS:
-                if k in st and st[k].dtype == torch.int32:
-                    st[k] = st[k].view(torch.float32)
+        """Load a state dict made by ``state_dict()``.  torch's own loader casts every
+        state tensor to its parameter's dtype, which would turn the uint8 codes and
+        fp32 block maxima into parameter-typed values; this one keeps their dtypes and
+        only moves them to the parameter's device."""
+        saved_groups = state_dict["param_groups"]
+        if len(saved_groups) != len(self.param_groups):
+            raise ValueError("state dict has a different number of parameter groups")
+        by_id = {}
+        for group, saved in zip(self.param_groups, saved_groups):
+            if len(group["params"]) != len(saved["params"]):
+                raise ValueError("state dict has a different number of parameters in a group")
+            by_id.update(zip(saved["params"], group["params"]))
+        state = defaultdict(dict)
+        for pid, st in state_dict["state"].items():
+            p = by_id[pid]
+            new = {k: (v.to(device=p.device) if torch.is_tensor(v) else v) for k, v in st.items()}
+            n = p.numel()
+            for k, dt, size in (("m_codes", torch.uint8, n), ("v_codes", torch.uint8, n),
+                                ("m_absmax", torch.float32, nblocks(n)),
+                                ("v_absmax", torch.float32, nblocks(n))):
+                t = new.get(k)
+                if t is None or t.dtype != dt or t.numel() != size:
+                    raise ValueError(f"state '{k}' of a parameter with {n} elements must be "
+                                     f"{dt} with {size} elements")
+            new["step"] = int(new["step"])
+            state[p] = new
+        self.state = state
+        for group, saved in zip(self.param_groups, saved_groups):
+            for k, v in saved.items():
+                if k != "params":
+                    group[k] = v
         self._prepared = {}

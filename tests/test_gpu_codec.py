@@ -110,14 +110,16 @@ def test_exhaustive_unit_interval(q, kind):
     x = torch.zeros(nblk * 2048, dtype=torch.float32, device="cuda")
     xv = x.view(nblk, 2048)
     xv[:, 0] = 1.0
-    body = xv[:, 1:].reshape(-1)
-    body[:N] = torch.arange(0, N, dtype=torch.int32, device="cuda").view(torch.float32)
+    sweep = torch.zeros(nblk * per, dtype=torch.float32, device="cuda")
+    sweep[:N] = torch.arange(0, N, dtype=torch.int32, device="cuda").view(torch.float32)
+    xv[:, 1:] = sweep.view(nblk, per)
+    del sweep
     T = oracle.code_transitions(kind)
     want_pos = T.view(np.uint32).astype(np.int64)          # sweep index == bit pattern
     nmag = T.size + 1
     for sign in ([1.0, -1.0] if kind == oracle.SIGNED else [1.0]):
         if sign < 0:
-            body[:N].neg_()
+            xv[:, 1:].neg_()
         codes, absmax = q.qopt_quantize_blockwise(x, kind)
         assert bool((absmax == 1.0).all())
         sc = codes.view(nblk, 2048)[:, 1:].reshape(-1)[:N]
