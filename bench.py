@@ -143,6 +143,31 @@ def calibrate_copy(torch, reps):
                       "bytes_written_per_copy": 4 * n, "copies": reps}), flush=True)
 
 
+def hbm_reference(torch, reps):
+    """Bandwidth of plain torch device operations on 8 GiB fp32 buffers: the
+    achievable-bandwidth reference the step is compared with."""
+    n = 1 << 31
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ops = {"copy_ (read + write)": (lambda: b.copy_(a), 8 * n),
+           "fill_ (write)": (lambda: b.fill_(2.0), 4 * n),
+           "sum (read)": (lambda: a.sum(), 4 * n)}
+    out = {}
+    for name, (fn, nbytes) in ops.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 3), "GB/s": round(nbytes / ms / 1e6, 1),
+                     "frac": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4)}
+    print(json.dumps({"hbm_reference": out, "buffer_bytes": 4 * n}), flush=True)
+
+
 def bench_codec(torch, workloads, q, args):
     """Block-wise quantize and dequantize of 2^28 values 0.01 * Student-t(3)."""
     n = 1 << 28
@@ -190,6 +215,8 @@ def main():
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "gpt1p3b", "flat20b", "codec256m"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hbm-reference", action="store_true",
+                    help="only time torch's copy_, fill_ and sum over 8 GiB buffers")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch copies of 4 GiB (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -205,6 +232,8 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         return calibrate_copy(torch, args.steps)
+    if args.hbm_reference:
+        return hbm_reference(torch, args.steps)
     if args.workload == "codec256m":
         return bench_codec(torch, workloads, q, args)
     log(f"building workload {args.workload}")
