@@ -180,18 +180,18 @@ def bench_codec(torch, workloads, q, args):
         q.qopt_quantize_blockwise(x, q.SIGNED, codes=codes, absmax=absmax)
         q.qopt_dequantize_blockwise(codes, absmax, q.SIGNED, out=y)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    tq = td = 0.0
-    for _ in range(args.steps):
-        ev[0].record()
-        q.qopt_quantize_blockwise(x, q.SIGNED, codes=codes, absmax=absmax)
-        ev[1].record()
-        q.qopt_dequantize_blockwise(codes, absmax, q.SIGNED, out=y)
-        ev[2].record()
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        tq += ev[0].elapsed_time(ev[1])
-        td += ev[1].elapsed_time(ev[2])
-    tq, td = tq / args.steps, td / args.steps
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    tq = timed(lambda: q.qopt_quantize_blockwise(x, q.SIGNED, codes=codes, absmax=absmax))
+    td = timed(lambda: q.qopt_dequantize_blockwise(codes, absmax, q.SIGNED, out=y))
     byts = n * 5 + (n // 2048) * 4
     out = {"metric": "block-wise dynamic-tree quantize + dequantize values/s at 1 GPU",
            "value": n / ((tq + td) * 1e-3), "unit": "values/s", "n_gpus": 1,

@@ -48,26 +48,43 @@ static_assert(kSlices * kWave * 4 == QOPT_BLOCK, "block layout");
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-#ifndef QOPT_NONTEMPORAL
-#define QOPT_NONTEMPORAL 1
+// Cache policy per stream, chosen by measurement on MI355X: the wide streams
+// (parameters, gradients, codec values) go non-temporal; the one-byte code streams
+// use ordinary cached accesses.
+#ifndef QOPT_NT_WIDE_LOAD
+#define QOPT_NT_WIDE_LOAD 1
+#endif
+#ifndef QOPT_NT_WIDE_STORE
+#define QOPT_NT_WIDE_STORE 1
+#endif
+#ifndef QOPT_NT_CODE_LOAD
+#define QOPT_NT_CODE_LOAD 0
+#endif
+#ifndef QOPT_NT_CODE_STORE
+#define QOPT_NT_CODE_STORE 0
 #endif
 
-template <typename T>
-__device__ __forceinline__ T ld_stream(const T* p) {
-#if QOPT_NONTEMPORAL
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
+template <bool kNt, typename T>
+__device__ __forceinline__ T ld_policy(const T* p) {
+  if constexpr (kNt) return __builtin_nontemporal_load(p);
+  else return *p;
 }
-
-template <typename T>
-__device__ __forceinline__ void st_stream(T* p, T v) {
-#if QOPT_NONTEMPORAL
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
-#endif
+template <bool kNt, typename T>
+__device__ __forceinline__ void st_policy(T* p, T v) {
+  if constexpr (kNt) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+template <typename T> __device__ __forceinline__ T ld_wide(const T* p) {
+  return ld_policy<QOPT_NT_WIDE_LOAD != 0>(p);
+}
+template <typename T> __device__ __forceinline__ void st_wide(T* p, T v) {
+  st_policy<QOPT_NT_WIDE_STORE != 0>(p, v);
+}
+template <typename T> __device__ __forceinline__ T ld_code(const T* p) {
+  return ld_policy<QOPT_NT_CODE_LOAD != 0>(p);
+}
+template <typename T> __device__ __forceinline__ void st_code(T* p, T v) {
+  st_policy<QOPT_NT_CODE_STORE != 0>(p, v);
 }
 
 // ------------------------------------------------------------------ helpers
@@ -87,16 +104,17 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  uint32_t b = __float_as_uint(x);
-  b += 0x7FFFu + ((b >> 16) & 1u);
-  return b >> 16;
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950; it
+// matches integer nearest-even rounding on every non-NaN binary32 input).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Per-codebook encoder parameters kept in registers for the whole kernel.
 struct Encoder {
   const qopt_codebook* cb;  // LDS copy
-  float a_floor;            // the binary32 whose key is key0
   uint32_t key0;
   uint32_t last_bucket;
 };
@@ -105,7 +123,6 @@ __device__ __forceinline__ Encoder make_encoder(const qopt_codebook* lds_cb) {
   Encoder e;
   e.cb = lds_cb;
   e.key0 = lds_cb->key0;
-  e.a_floor = __uint_as_float(e.key0 << 15);
   uint32_t nb = lds_cb->nbuckets;
   nb = nb < 1u ? 1u : (nb > QOPT_MAX_BUCKETS ? QOPT_MAX_BUCKETS : nb);
   e.last_bucket = nb - 1;
@@ -113,13 +130,12 @@ __device__ __forceinline__ Encoder make_encoder(const qopt_codebook* lds_cb) {
 }
 
 // Magnitude index of a >= 0: bucket start index, plus one if a reaches the single
-// threshold that may lie inside the bucket.  Values below bucket 0 (and NaN) are
-// raised to its start, values above the last bucket are clamped to it, so every
-// index stays inside the tables for any table contents (bucket bytes <= 255,
-// thresh has >= 257 entries).
+// threshold that may lie inside the bucket.  The bucket index saturates at 0 below
+// bucket 0 and is clamped to the last bucket above it, so every index stays inside
+// the tables for any input and any table contents (bucket bytes <= 255, thresh has
+// >= 257 entries).
 __device__ __forceinline__ uint32_t encode_mag(const Encoder& e, float a) {
-  const float ac = fmaxf(a, e.a_floor);
-  uint32_t i = (__float_as_uint(ac) >> 15) - e.key0;
+  uint32_t i = __builtin_elementwise_sub_sat(__float_as_uint(a) >> 15, e.key0);
   i = i < e.last_bucket ? i : e.last_bucket;
   const uint32_t b = e.cb->bucket[i];
   return b + (a >= e.cb->thresh[b + 1] ? 1u : 0u);
@@ -145,6 +161,11 @@ __device__ __forceinline__ uint32_t encode_signed(const Encoder& e, const BlockS
   return encode_mag(e, fabsf(x) * s.r) | (x < 0.0f ? s.sign_mask : 0u);
 }
 
+// Second moments are sums of non-negative terms, so no sign bit is ever set.
+__device__ __forceinline__ uint32_t encode_nonneg(const Encoder& e, const BlockScale& s, float x) {
+  return encode_mag(e, x * s.r);
+}
+
 // ---------------------------------------------------------- codec kernels
 
 struct CodecArgs {
@@ -160,6 +181,7 @@ struct CodecArgs {
   uint32_t vector_ok;     // pointers allow the vector path for full blocks
 };
 
+// Quantize: the wave loads its next block while it encodes the current one.
 __global__ void __launch_bounds__(kThreads)
 quantize_kernel(CodecArgs a) {
   __shared__ __align__(16) qopt_codebook cb;
@@ -171,17 +193,28 @@ quantize_kernel(CodecArgs a) {
   const int lane = threadIdx.x % kWave;
   const uint32_t stride = gridDim.x * kWaves;
 
-  for (uint32_t blk = blockIdx.x * kWaves + wave; blk < a.nblocks; blk += stride) {
+  uint32_t blk = blockIdx.x * kWaves + wave;
+  if (blk >= a.nblocks) return;
+  auto block_len = [&](uint32_t b) {
+    const int64_t rem = a.n - static_cast<int64_t>(b) * QOPT_BLOCK;
+    return rem < QOPT_BLOCK ? static_cast<int>(rem) : QOPT_BLOCK;
+  };
+  auto load_vec = [&](uint32_t b, f32x4 X[kSlices]) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(a.x + static_cast<int64_t>(b) * QOPT_BLOCK);
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) X[s] = ld_wide(src + s * kWave + lane);
+  };
+  int len = block_len(blk);
+  bool vec = len == QOPT_BLOCK && a.vector_ok;
+  f32x4 X[kSlices];
+  if (vec) load_vec(blk, X);
+  for (;;) {
     const int64_t base = static_cast<int64_t>(blk) * QOPT_BLOCK;
-    const int64_t rem = a.n - base;
-    const int len = rem < QOPT_BLOCK ? static_cast<int>(rem) : QOPT_BLOCK;
     float x[kSlices][4];
-    if (len == QOPT_BLOCK && a.vector_ok) {
-      const f32x4* src = reinterpret_cast<const f32x4*>(a.x + base);
+    if (vec) {
 #pragma unroll
       for (int s = 0; s < kSlices; ++s) {
-        const f32x4 v = ld_stream(src + s * kWave + lane);
-        x[s][0] = v.x; x[s][1] = v.y; x[s][2] = v.z; x[s][3] = v.w;
+        x[s][0] = X[s].x; x[s][1] = X[s].y; x[s][2] = X[s].z; x[s][3] = X[s].w;
       }
     } else {
 #pragma unroll
@@ -199,14 +232,24 @@ quantize_kernel(CodecArgs a) {
       for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(x[s][j]));
     const BlockScale sc = block_scale(wave_max(amax), sign_mask);
 
-    if (len == QOPT_BLOCK && a.vector_ok) {
+    const uint32_t nblk = blk + stride;
+    const bool more = nblk < a.nblocks;
+    int nlen = len;
+    bool nvec = false;
+    if (more) {
+      nlen = block_len(nblk);
+      nvec = nlen == QOPT_BLOCK && a.vector_ok;
+      if (nvec) load_vec(nblk, X);
+    }
+
+    if (vec) {
       uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes_out + base);
 #pragma unroll
       for (int s = 0; s < kSlices; ++s) {
         uint32_t w = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) w |= encode_signed(enc, sc, x[s][j]) << (8 * j);
-        st_stream(dst + s * kWave + lane, w);
+        st_code(dst + s * kWave + lane, w);
       }
     } else {
 #pragma unroll
@@ -218,6 +261,10 @@ quantize_kernel(CodecArgs a) {
         }
     }
     if (lane == 0) a.absmax_out[blk] = sc.absmax;
+    if (!more) break;
+    blk = nblk;
+    len = nlen;
+    vec = nvec;
   }
 }
 
@@ -240,7 +287,7 @@ dequantize_kernel(CodecArgs a) {
       f32x4* dst = reinterpret_cast<f32x4*>(a.y + base);
       uint32_t w[kSlices];
 #pragma unroll
-      for (int s = 0; s < kSlices; ++s) w[s] = ld_stream(src + s * kWave + lane);
+      for (int s = 0; s < kSlices; ++s) w[s] = ld_code(src + s * kWave + lane);
 #pragma unroll
       for (int s = 0; s < kSlices; ++s) {
         f32x4 v;
@@ -248,7 +295,7 @@ dequantize_kernel(CodecArgs a) {
         v.y = cb.decode[(w[s] >> 8) & 0xFFu] * A;
         v.z = cb.decode[(w[s] >> 16) & 0xFFu] * A;
         v.w = cb.decode[w[s] >> 24] * A;
-        st_stream(dst + s * kWave + lane, v);
+        st_wide(dst + s * kWave + lane, v);
       }
     } else {
 #pragma unroll
@@ -302,8 +349,8 @@ __device__ __forceinline__ void pack4(const float in[4], f32x4& v) {
   v.x = in[0]; v.y = in[1]; v.z = in[2]; v.w = in[3];
 }
 __device__ __forceinline__ void pack4(const float in[4], u32x2& v) {
-  v.x = f32_to_bf16_rne(in[0]) | (f32_to_bf16_rne(in[1]) << 16);
-  v.y = f32_to_bf16_rne(in[2]) | (f32_to_bf16_rne(in[3]) << 16);
+  v.x = pack_bf16x2(in[0], in[1]);
+  v.y = pack_bf16x2(in[2], in[3]);
 }
 
 template <typename T> __device__ __forceinline__ float load1(const void* p, int64_t i);
@@ -318,7 +365,7 @@ template <> __device__ __forceinline__ void store1<float>(void* p, int64_t i, fl
   static_cast<float*>(p)[i] = x;
 }
 template <> __device__ __forceinline__ void store1<uint16_t>(void* p, int64_t i, float x) {
-  static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(f32_to_bf16_rne(x));
+  static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xFFFFu);
 }
 
 // One element of the update; returns the new parameter, leaves m and v.
@@ -390,10 +437,10 @@ __device__ __forceinline__ void load_block(BlockIn<PT, GT>& in, const BlockRef& 
 #pragma unroll
   for (int s = 0; s < kSlices; ++s) {
     const int idx = s * kWave + lane;
-    in.p[s] = ld_stream(p + idx);
-    in.g[s] = ld_stream(g + idx);
-    in.cm[s] = ld_stream(cm + idx);
-    in.cv[s] = ld_stream(cv + idx);
+    in.p[s] = ld_wide(p + idx);
+    in.g[s] = ld_wide(g + idx);
+    in.cm[s] = ld_code(cm + idx);
+    in.cv[s] = ld_code(cv + idx);
   }
 }
 
@@ -420,7 +467,7 @@ __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_code
     }
     PV pv;
     pack4(p4, pv);
-    st_stream(pout + s * kWave + lane, pv);
+    st_wide(pout + s * kWave + lane, pv);
   }
 }
 
@@ -468,11 +515,11 @@ __device__ __forceinline__ void requantize(const Encoder& em, const Encoder& ev,
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       wm |= encode_signed(em, sm, m[s][j]) << (8 * j);
-      wv |= encode_signed(ev, sv, v[s][j]) << (8 * j);
+      wv |= encode_nonneg(ev, sv, v[s][j]) << (8 * j);
     }
     if (r.vec) {
-      st_stream(cmo + s * kWave + lane, wm);
-      st_stream(cvo + s * kWave + lane, wv);
+      st_code(cmo + s * kWave + lane, wm);
+      st_code(cvo + s * kWave + lane, wv);
       } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
