@@ -378,6 +378,24 @@ __device__ __forceinline__ float adam_element(const AdamScalars& k, float p, flo
   return p - (k.step_size * u);
 }
 
+// Correctly rounded square root for x in {+0} U [2^-96, +inf]: the hardware estimate
+// is within one ulp, and a residual test against each neighbour picks the nearest
+// binary32.  This is sqrtf's own refinement without its rescaling of tiny inputs and
+// its special-case select, which are not needed on that range (checked bit for bit
+// against sqrtf on every binary32 in it).
+__device__ __forceinline__ float sqrt_rn_unscaled(float x) {
+  const float s = __builtin_amdgcn_sqrtf(x);
+  const float s_dn = __uint_as_float(__float_as_uint(s) - 1u);
+  const float s_up = __uint_as_float(__float_as_uint(s) + 1u);
+  const float r_dn = __builtin_fmaf(-s_dn, s, x);
+  const float r_up = __builtin_fmaf(-s_up, s, x);
+  float r = (r_dn <= 0.0f) ? s_dn : s;
+  r = (r_up > 0.0f) ? s_up : r;
+  return r;
+}
+
+constexpr float kTinyMoment = 0x1p-96f;  // below this, sqrt_rn_unscaled is not exact
+
 // Where one block lives, resolved from the launch's piece table (wave-uniform).
 struct BlockRef {
   void* param;
@@ -457,11 +475,32 @@ __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_code
     float p4[4], g4[4];
     unpack4(in.p[s], p4);
     unpack4(in.g[s], g4);
+    // the moments of the slice's 4 elements, then their square roots: the short
+    // sequence unless some lane of the wave holds a tiny second moment
+    float sq[4];
+    uint64_t tiny = 0;  // lanes (as a wave mask) holding 0 < v < 2^-96
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float m_prev = cbm.decode[(in.cm[s] >> (8 * j)) & 0xFFu] * in.am;
       const float v_prev = cbv.decode[(in.cv[s] >> (8 * j)) & 0xFFu] * in.av;
-      p4[j] = adam_element(k, p4[j], g4[j], m_prev, v_prev, m[s][j], v[s][j]);
+      m[s][j] = (k.b1 * m_prev) + (k.omb1 * g4[j]);
+      v[s][j] = (k.b2 * v_prev) + (k.omb2 * (g4[j] * g4[j]));
+      // 0 < v < 2^-96 as one unsigned compare on the bits (v is never negative)
+      tiny |= __builtin_amdgcn_ballot_w64((__float_as_uint(v[s][j]) - 1u) <
+                                          (__float_as_uint(kTinyMoment) - 1u));
+    }
+    if (tiny != 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sq[j] = sqrtf(v[s][j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sq[j] = sqrt_rn_unscaled(v[s][j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float denom = (sq[j] * k.inv_sqrt_bc2) + k.eps;
+      const float u = m[s][j] / denom;
+      p4[j] = p4[j] - (k.step_size * u);
       mmax = fmaxf(mmax, fabsf(m[s][j]));
       vmax = fmaxf(vmax, v[s][j]);
     }

@@ -97,9 +97,10 @@ def host_params(n, pdt, rng):
     return oracle.f32_to_bf16_rne(p) if pdt == "bf16" else p
 
 
-def run_small(q, sizes, pdt, gdt, steps, seed, hp=HP, views=None):
+def run_small(q, sizes, pdt, gdt, steps, seed, hp=HP, views=None, grads=None):
     """Full-element parity over a list of tensors for several steps."""
     rng = np.random.default_rng(seed)
+    grads = grads or host_grads
     hp_p = [host_params(n, pdt, rng) for n in sizes]
     hs = [host_state(n) for n in sizes]
     if views is None:
@@ -108,7 +109,7 @@ def run_small(q, sizes, pdt, gdt, steps, seed, hp=HP, views=None):
     else:
         dp, ds = views(hp_p)
     for step in range(1, steps + 1):
-        hg = [host_grads(n, gdt, rng) for n in sizes]
+        hg = [grads(n, gdt, rng) for n in sizes]
         dg = [to_dev(g, gdt) for g in hg]
         q.qopt_adam8bit_step([(dp[i], dg[i], *ds[i]) for i in range(len(sizes))],
                              step=step, **hp)
@@ -190,6 +191,21 @@ def test_misaligned_views(q):
 def test_other_hyperparameters(q, hp):
     say(f"hyper-parameters {hp}")
     run_small(q, [2048 * 3 + 100], "f32", "f32", steps=4, seed=6, hp=hp)
+
+
+@pytest.mark.parametrize("pdt,gdt", [("f32", "f32"), ("bf16", "bf16")])
+def test_tiny_second_moments(q, pdt, gdt):
+    """Gradients from 1e-30 to 1e-3 within and across blocks: second moments in
+    (0, 2^-96), subnormal ones, exact zeros and ordinary ones, so both square-root
+    branches of the kernel run, in the same wave and in separate waves."""
+    def grads(n, gdt_, rng):
+        mag = 10.0 ** rng.uniform(-30, -3, n)
+        g = (rng.choice([-1.0, 1.0], n) * mag).astype(np.float32)
+        g[: 2048] = (1e-18 * rng.standard_normal(2048)).astype(np.float32)  # v subnormal
+        g[2048: 2048 + 64] = 0.0
+        return oracle.f32_to_bf16_rne(g) if gdt_ == "bf16" else g
+    say(f"tiny second moments {pdt}/{gdt}")
+    run_small(q, [4 * 2048 + 77], pdt, gdt, steps=3, seed=11, grads=grads)
 
 
 def test_late_step_and_zero_blocks(q):
