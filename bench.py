@@ -207,13 +207,76 @@ def bench_codec(torch, workloads, q, args):
     print(json.dumps(out), flush=True)
 
 
+def bench_convert(torch, workloads, q, args):
+    """Checkpoint moment codec on the Llama-7B set: fp32 Adam moments (m, v) of all
+    291 tensors -> block-wise 8-bit state, and back, with preallocated outputs."""
+    sizes = [n for _, n in workloads.llama7b_shapes()]
+    total = sum(sizes)
+    M = torch.empty(total, dtype=torch.float32, device="cuda")
+    V = torch.empty(total, dtype=torch.float32, device="cuda")
+    workloads.fill_normal_(M, 1e-4, 71)
+    workloads.fill_normal_(V, 1e-4, 72)
+    V.square_()
+    CM = torch.empty(total, dtype=torch.uint8, device="cuda")
+    CV = torch.empty_like(CM)
+    nbs = [-(-n // 2048) for n in sizes]
+    AM = torch.empty(sum(nbs), dtype=torch.float32, device="cuda")
+    AV = torch.empty_like(AM)
+    views, off, boff = [], 0, 0
+    for n, nb in zip(sizes, nbs):
+        views.append((slice(off, off + n), slice(boff, boff + nb)))
+        off += n
+        boff += nb
+
+    m_set = [(M[s], CM[s], AM[bs]) for s, bs in views]
+    v_set = [(V[s], CV[s], AV[bs]) for s, bs in views]
+
+    def compress():
+        q.qopt_quantize_blockwise_multi(m_set, q.SIGNED)
+        q.qopt_quantize_blockwise_multi(v_set, q.UNSIGNED)
+
+    def decompress():
+        q.qopt_dequantize_blockwise_multi(m_set, q.SIGNED)
+        q.qopt_dequantize_blockwise_multi(v_set, q.UNSIGNED)
+
+    def timed(fn):
+        for _ in range(args.warmup + 1):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    tc = timed(compress)
+    td = timed(decompress)
+    nb_total = sum(nbs)
+    byts = 2 * (total * 5 + nb_total * 4)   # each direction, both moments
+    out = {"metric": "fp32 Adam moments <-> block-wise 8-bit state conversion, params/s at 1 GPU",
+           "value": total / ((tc + td) * 1e-3), "unit": "params/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tc + td, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": "convert7b: m ~ N(0,1e-4), v = N(0,1e-4)^2 for the 291 tensors "
+                                  "of the Llama-7B set (6,738,415,616 params), multi-tensor "
+                                  "codec calls"},
+           "kernels": {"compress": {"ms": round(tc, 3), "GB/s": round(byts / tc / 1e6, 1),
+                                    "frac": round(byts / tc / 1e6 / HBM_PEAK_GBS, 4)},
+                       "decompress": {"ms": round(td, 3), "GB/s": round(byts / td / 1e6, 1),
+                                      "frac": round(byts / td / 1e6 / HBM_PEAK_GBS, 4)}}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "gpt1p3b", "flat20b", "codec256m"])
+                    choices=["llama7b", "gpt1p3b", "flat20b", "codec256m", "convert7b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hbm-reference", action="store_true",
                     help="only time torch's copy_, fill_ and sum over 8 GiB buffers")
@@ -236,6 +299,8 @@ def main():
         return hbm_reference(torch, args.steps)
     if args.workload == "codec256m":
         return bench_codec(torch, workloads, q, args)
+    if args.workload == "convert7b":
+        return bench_convert(torch, workloads, q, args)
     log(f"building workload {args.workload}")
     tensors, sizes, pdt, gdt, label = make_workload(args.workload, torch, workloads)
     prepared = q.make_tensor_array(tensors)

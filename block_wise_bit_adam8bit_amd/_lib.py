@@ -58,6 +58,15 @@ class qopt_tensor(ctypes.Structure):
     ]
 
 
+class qopt_codec_tensor(ctypes.Structure):
+    _fields_ = [
+        ("values", ctypes.c_void_p),
+        ("codes", ctypes.c_void_p),
+        ("absmax", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+    ]
+
+
 class qopt_adam_hparams(ctypes.Structure):
     _fields_ = [
         ("lr", ctypes.c_float),
@@ -75,6 +84,12 @@ _SIGNATURES = {
     "qopt_dequantize_blockwise": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_void_p, ctypes.c_int64,
                                                  ctypes.c_void_p, ctypes.c_void_p]),
+    "qopt_quantize_blockwise_multi": (ctypes.c_int, [ctypes.c_void_p,
+                                                     ctypes.POINTER(qopt_codec_tensor),
+                                                     ctypes.c_int32, ctypes.c_void_p]),
+    "qopt_dequantize_blockwise_multi": (ctypes.c_int, [ctypes.c_void_p,
+                                                       ctypes.POINTER(qopt_codec_tensor),
+                                                       ctypes.c_int32, ctypes.c_void_p]),
     "qopt_adam8bit_step": (ctypes.c_int, [ctypes.POINTER(qopt_tensor), ctypes.c_int32,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.POINTER(qopt_adam_hparams),

@@ -168,50 +168,111 @@ __device__ __forceinline__ uint32_t encode_nonneg(const Encoder& e, const BlockS
 
 // ---------------------------------------------------------- codec kernels
 
-struct CodecArgs {
-  const qopt_codebook* cb;
-  const float* x;         // quantize input / dequantize output
-  float* y;
-  const uint8_t* codes_in;
-  uint8_t* codes_out;
-  const float* absmax_in;
-  float* absmax_out;
-  int64_t n;
-  uint32_t nblocks;
-  uint32_t vector_ok;     // pointers allow the vector path for full blocks
+// Index of the last piece whose first block is <= blk, by a fixed six-step search
+// (kMaxTensors <= 64) written without a loop: a loop here, inside the kernels' block
+// loops, measurably slows them even when it rarely runs.
+static_assert(kMaxTensors <= 64, "piece search depth");
+__device__ __forceinline__ uint32_t piece_of(const uint32_t* block_start, uint32_t npieces,
+                                             uint32_t blk) {
+  uint32_t t = 0;
+#pragma unroll
+  for (uint32_t s = 32; s > 0; s >>= 1) {
+    const uint32_t probe = t + s;
+    if (probe < npieces && block_start[probe] <= blk) t = probe;
+  }
+  return t;
+}
+
+// One codec launch's work: up to kMaxTensors pieces, each a run of whole blocks of
+// one tensor (the same plan as the step's, see plan_chunks).
+struct CodecChunk {
+  float* vals[kMaxTensors];               // quantize: input; dequantize: output
+  uint8_t* codes[kMaxTensors];
+  float* absmax[kMaxTensors];
+  int64_t n[kMaxTensors];
+  uint32_t block_lo[kMaxTensors];
+  uint32_t block_start[kMaxTensors + 1];
+  uint32_t npieces;
+  uint64_t vector_ok;                     // bit i: piece i may use the vector path
 };
 
-// Quantize: the wave loads its next block while it encodes the current one.
+// The piece a wave is working in, held in scalar registers: consecutive blocks of a
+// wave usually fall in the same piece, so the piece table is only searched again
+// when the grid stride leaves it.
+struct CodecPiece {
+  float* vals;
+  uint8_t* codes;
+  float* absmax;
+  int64_t n;
+  uint32_t begin, end;  // launch-wide block range of the piece
+  uint32_t lo;          // the piece's first block within its tensor
+  uint32_t vec_ok;
+};
+
+__device__ __forceinline__ CodecPiece find_piece(const CodecChunk& c, uint32_t blk) {
+  const uint32_t lo = piece_of(c.block_start, c.npieces, blk);
+  CodecPiece pc;
+  pc.vals = c.vals[lo];
+  pc.codes = c.codes[lo];
+  pc.absmax = c.absmax[lo];
+  pc.n = c.n[lo];
+  pc.begin = c.block_start[lo];
+  pc.end = c.block_start[lo + 1];
+  pc.lo = c.block_lo[lo];
+  pc.vec_ok = static_cast<uint32_t>((c.vector_ok >> lo) & 1u);
+  return pc;
+}
+
+struct CodecRef {
+  float* vals;
+  uint8_t* codes;
+  float* absmax;  // this block's entry
+  int64_t base;
+  int len;
+  uint32_t vec;
+};
+
+__device__ __forceinline__ CodecRef block_of(const CodecPiece& pc, uint32_t blk) {
+  const uint32_t lb = pc.lo + (blk - pc.begin);
+  CodecRef r;
+  r.vals = pc.vals;
+  r.codes = pc.codes;
+  r.absmax = pc.absmax + lb;
+  r.base = static_cast<int64_t>(lb) * QOPT_BLOCK;
+  const int64_t rem = pc.n - r.base;
+  r.len = rem < QOPT_BLOCK ? static_cast<int>(rem) : QOPT_BLOCK;
+  r.vec = (r.len == QOPT_BLOCK && pc.vec_ok) ? 1u : 0u;
+  return r;
+}
+
+// Quantize: each wave walks blocks with a grid stride and loads its next block while
+// it encodes the current one.
 __global__ void __launch_bounds__(kThreads)
-quantize_kernel(CodecArgs a) {
+quantize_kernel(CodecChunk c, const qopt_codebook* cb_g) {
   __shared__ __align__(16) qopt_codebook cb;
-  stage_codebook(&cb, a.cb);
+  stage_codebook(&cb, cb_g);
   __syncthreads();
   const Encoder enc = make_encoder(&cb);
   const uint32_t sign_mask = cb.sign_mask;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const uint32_t stride = gridDim.x * kWaves;
+  const uint32_t total = c.block_start[c.npieces];
 
   uint32_t blk = blockIdx.x * kWaves + wave;
-  if (blk >= a.nblocks) return;
-  auto block_len = [&](uint32_t b) {
-    const int64_t rem = a.n - static_cast<int64_t>(b) * QOPT_BLOCK;
-    return rem < QOPT_BLOCK ? static_cast<int>(rem) : QOPT_BLOCK;
-  };
-  auto load_vec = [&](uint32_t b, f32x4 X[kSlices]) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(a.x + static_cast<int64_t>(b) * QOPT_BLOCK);
+  if (blk >= total) return;
+  auto load_vec = [&](const CodecRef& r, f32x4 X[kSlices]) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(r.vals + r.base);
 #pragma unroll
     for (int s = 0; s < kSlices; ++s) X[s] = ld_wide(src + s * kWave + lane);
   };
-  int len = block_len(blk);
-  bool vec = len == QOPT_BLOCK && a.vector_ok;
+  CodecPiece piece = find_piece(c, blk);
+  CodecRef cur = block_of(piece, blk);
   f32x4 X[kSlices];
-  if (vec) load_vec(blk, X);
+  if (cur.vec) load_vec(cur, X);
   for (;;) {
-    const int64_t base = static_cast<int64_t>(blk) * QOPT_BLOCK;
     float x[kSlices][4];
-    if (vec) {
+    if (cur.vec) {
 #pragma unroll
       for (int s = 0; s < kSlices; ++s) {
         x[s][0] = X[s].x; x[s][1] = X[s].y; x[s][2] = X[s].z; x[s][3] = X[s].w;
@@ -222,7 +283,7 @@ quantize_kernel(CodecArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = s * 256 + lane * 4 + j;
-          x[s][j] = e < len ? a.x[base + e] : 0.0f;
+          x[s][j] = e < cur.len ? cur.vals[cur.base + e] : 0.0f;
         }
     }
     float amax = 0.0f;
@@ -233,17 +294,16 @@ quantize_kernel(CodecArgs a) {
     const BlockScale sc = block_scale(wave_max(amax), sign_mask);
 
     const uint32_t nblk = blk + stride;
-    const bool more = nblk < a.nblocks;
-    int nlen = len;
-    bool nvec = false;
+    const bool more = nblk < total;
+    CodecRef nxt = cur;
     if (more) {
-      nlen = block_len(nblk);
-      nvec = nlen == QOPT_BLOCK && a.vector_ok;
-      if (nvec) load_vec(nblk, X);
+      if (nblk >= piece.end) piece = find_piece(c, nblk);
+      nxt = block_of(piece, nblk);
+      if (nxt.vec) load_vec(nxt, X);
     }
 
-    if (vec) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes_out + base);
+    if (cur.vec) {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(cur.codes + cur.base);
 #pragma unroll
       for (int s = 0; s < kSlices; ++s) {
         uint32_t w = 0;
@@ -257,34 +317,37 @@ quantize_kernel(CodecArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = s * 256 + lane * 4 + j;
-          if (e < len) a.codes_out[base + e] = static_cast<uint8_t>(encode_signed(enc, sc, x[s][j]));
+          if (e < cur.len)
+            cur.codes[cur.base + e] = static_cast<uint8_t>(encode_signed(enc, sc, x[s][j]));
         }
     }
-    if (lane == 0) a.absmax_out[blk] = sc.absmax;
+    if (lane == 0) *cur.absmax = sc.absmax;
     if (!more) break;
     blk = nblk;
-    len = nlen;
-    vec = nvec;
+    cur = nxt;
   }
 }
 
 __global__ void __launch_bounds__(kThreads)
-dequantize_kernel(CodecArgs a) {
+dequantize_kernel(CodecChunk c, const qopt_codebook* cb_g) {
   __shared__ __align__(16) qopt_codebook cb;
-  stage_codebook(&cb, a.cb);
+  stage_codebook(&cb, cb_g);
   __syncthreads();
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const uint32_t stride = gridDim.x * kWaves;
+  const uint32_t total = c.block_start[c.npieces];
 
-  for (uint32_t blk = blockIdx.x * kWaves + wave; blk < a.nblocks; blk += stride) {
-    const int64_t base = static_cast<int64_t>(blk) * QOPT_BLOCK;
-    const int64_t rem = a.n - base;
-    const int len = rem < QOPT_BLOCK ? static_cast<int>(rem) : QOPT_BLOCK;
-    const float A = a.absmax_in[blk];
-    if (len == QOPT_BLOCK && a.vector_ok) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(a.codes_in + base);
-      f32x4* dst = reinterpret_cast<f32x4*>(a.y + base);
+  uint32_t blk = blockIdx.x * kWaves + wave;
+  if (blk >= total) return;
+  CodecPiece piece = find_piece(c, blk);
+  for (; blk < total; blk += stride) {
+    if (blk >= piece.end) piece = find_piece(c, blk);
+    const CodecRef r = block_of(piece, blk);
+    const float A = *r.absmax;
+    if (r.vec) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(r.codes + r.base);
+      f32x4* dst = reinterpret_cast<f32x4*>(r.vals + r.base);
       uint32_t w[kSlices];
 #pragma unroll
       for (int s = 0; s < kSlices; ++s) w[s] = ld_code(src + s * kWave + lane);
@@ -303,7 +366,7 @@ dequantize_kernel(CodecArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int e = s * 256 + lane * 4 + j;
-          if (e < len) a.y[base + e] = cb.decode[a.codes_in[base + e]] * A;
+          if (e < r.len) r.vals[r.base + e] = cb.decode[r.codes[r.base + e]] * A;
         }
     }
   }
@@ -406,16 +469,14 @@ struct BlockRef {
   float* av;
   int64_t base;  // first element of the block within its tensor
   int len;       // elements in the block (2048 except a tensor's last block)
-  bool vec;      // full block of a tensor whose pointers allow vector accesses
+  uint32_t vec;  // full block of a tensor whose pointers allow vector accesses
+  // (no bool and no tail padding here or in the other loop-carried descriptors:
+  // copying padding bytes keeps a private object alive that the compiler then
+  // moves to LDS, adding LDS traffic to the block loop)
 };
 
 __device__ __forceinline__ BlockRef resolve(const StepChunk& c, uint32_t blk) {
-  uint32_t lo = 0, hi = c.npieces;  // last piece t with block_start[t] <= blk
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) / 2;
-    if (c.block_start[mid] <= blk) lo = mid; else hi = mid;
-  }
-  const uint32_t t = lo;
+  const uint32_t t = piece_of(c.block_start, c.npieces, blk);
   const uint32_t lb = c.block_lo[t] + (blk - c.block_start[t]);
   BlockRef r;
   r.param = c.param[t];
@@ -427,7 +488,7 @@ __device__ __forceinline__ BlockRef resolve(const StepChunk& c, uint32_t blk) {
   r.base = static_cast<int64_t>(lb) * QOPT_BLOCK;
   const int64_t rem = c.n[t] - r.base;
   r.len = rem < QOPT_BLOCK ? static_cast<int>(rem) : QOPT_BLOCK;
-  r.vec = r.len == QOPT_BLOCK && ((c.vector_ok >> t) & 1u);
+  r.vec = (r.len == QOPT_BLOCK && ((c.vector_ok >> t) & 1u)) ? 1u : 0u;
   return r;
 }
 
@@ -683,26 +744,26 @@ double pow_by_squaring(double b, int64_t t) {
 
 bool finite(float x) { return x == x && x - x == 0.0f; }
 
-// Splits the step into launches of equal block counts (the last may be shorter),
-// each holding at most kMaxTensors pieces.  For a given launch count the pieces
-// are assigned greedily in tensor order; the count grows until every launch fits.
-// emit(chunk, blocks) is called once per launch; returns the first error.
-template <typename Emit>
-int plan_chunks(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size_t gsize,
-                uint64_t nchunks, uint64_t total, Emit&& emit, bool* fits) {
+// Splits a list of tensors into launches of equal block counts (the last may be
+// shorter), each holding at most kMaxTensors pieces; a piece is a run of whole blocks
+// of one tensor.  For a given launch count the pieces are assigned greedily in
+// tensor order.  size_of(i) gives tensor i's length; fill(chunk, slot, i) writes its
+// pointers and length into the slot and says whether it may take the vector path;
+// emit(chunk, blocks) is called once per launch.  Returns the first error.
+template <typename Chunk, typename SizeOf, typename Fill, typename Emit>
+int plan_chunks(int32_t ntensors, const SizeOf& size_of, const Fill& fill, uint64_t nchunks,
+                uint64_t total, Emit&& emit, bool* fits) {
   const uint64_t target = (total + nchunks - 1) / nchunks;
-  StepChunk c;
+  Chunk c;
   c.npieces = 0;
   c.vector_ok = 0;
   c.block_start[0] = 0;
   uint64_t blocks = 0;
   *fits = true;
   for (int32_t i = 0; i < ntensors; ++i) {
-    const qopt_tensor& t = tensors[i];
-    if (t.n == 0) continue;
-    const uint64_t nb = (static_cast<uint64_t>(t.n) + QOPT_BLOCK - 1) / QOPT_BLOCK;
-    const bool vec = aligned(t.param, 4 * psize) && aligned(t.grad, 4 * gsize) &&
-                     aligned(t.m_codes, 4) && aligned(t.v_codes, 4);
+    const int64_t n = size_of(i);
+    if (n == 0) continue;
+    const uint64_t nb = (static_cast<uint64_t>(n) + QOPT_BLOCK - 1) / QOPT_BLOCK;
     uint64_t lo = 0;
     while (lo < nb) {
       if (c.npieces == static_cast<uint32_t>(kMaxTensors)) {
@@ -711,15 +772,8 @@ int plan_chunks(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size
       }
       const uint64_t take = (nb - lo < target - blocks) ? nb - lo : target - blocks;
       const uint32_t slot = c.npieces++;
-      c.param[slot] = t.param;
-      c.grad[slot] = t.grad;
-      c.m_codes[slot] = t.m_codes;
-      c.v_codes[slot] = t.v_codes;
-      c.m_absmax[slot] = t.m_absmax;
-      c.v_absmax[slot] = t.v_absmax;
-      c.n[slot] = t.n;
+      if (fill(c, slot, i)) c.vector_ok |= uint64_t{1} << slot;
       c.block_lo[slot] = static_cast<uint32_t>(lo);
-      if (vec) c.vector_ok |= uint64_t{1} << slot;
       blocks += take;
       lo += take;
       c.block_start[slot + 1] = static_cast<uint32_t>(blocks);
@@ -736,13 +790,16 @@ int plan_chunks(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size
   return QOPT_OK;
 }
 
-// Number of launches of one step over `tensors` (see plan_chunks).
-int count_chunks(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size_t gsize,
+// Launch count of the plan: the smallest count (from the piece bound up) whose
+// greedy assignment keeps every launch within kMaxTensors pieces and 2^31 blocks.
+template <typename Chunk, typename SizeOf, typename Fill>
+int count_chunks(int32_t ntensors, const SizeOf& size_of, const Fill& fill,
                  uint64_t* nchunks_out, uint64_t* total_out) {
   uint64_t total = 0, pieces = 0;
   for (int32_t i = 0; i < ntensors; ++i) {
-    if (tensors[i].n == 0) continue;
-    const uint64_t nb = (static_cast<uint64_t>(tensors[i].n) + QOPT_BLOCK - 1) / QOPT_BLOCK;
+    const int64_t n = size_of(i);
+    if (n == 0) continue;
+    const uint64_t nb = (static_cast<uint64_t>(n) + QOPT_BLOCK - 1) / QOPT_BLOCK;
     if (nb > 0xFFFFFFFFull) return QOPT_EINVAL;  // block index of one tensor is 32-bit
     total += nb;
     ++pieces;
@@ -750,39 +807,85 @@ int count_chunks(const qopt_tensor* tensors, int32_t ntensors, size_t psize, siz
   *total_out = total;
   *nchunks_out = 0;
   if (total == 0) return QOPT_OK;
-  // launches hold < 2^31 blocks and at most kMaxTensors pieces each
   uint64_t nchunks = (pieces + kMaxTensors - 1) / kMaxTensors;
   const uint64_t by_size = (total + 0x7FFFFFFFull - 1) / 0x7FFFFFFFull;
   if (nchunks < by_size) nchunks = by_size;
   for (;; ++nchunks) {
     bool fits = false;
-    plan_chunks(tensors, ntensors, psize, gsize, nchunks, total,
-                [](const StepChunk&, uint64_t) { return static_cast<int>(QOPT_OK); }, &fits);
+    plan_chunks<Chunk>(ntensors, size_of, fill, nchunks, total,
+                       [](const Chunk&, uint64_t) { return static_cast<int>(QOPT_OK); }, &fits);
     if (fits) break;
   }
   *nchunks_out = nchunks;
   return QOPT_OK;
 }
 
+// Plans and launches `kernel` over the tensors, one launch per chunk of the plan.
+template <typename Chunk, typename Kernel, typename SizeOf, typename Fill, typename... Args>
+int launch_planned(Kernel kernel, int32_t ntensors, const SizeOf& size_of, const Fill& fill,
+                   hipStream_t stream, Args... args) {
+  uint64_t nchunks = 0, total = 0;
+  int rc = count_chunks<Chunk>(ntensors, size_of, fill, &nchunks, &total);
+  if (rc != QOPT_OK || total == 0) return rc;
+  bool fits = true;
+  return plan_chunks<Chunk>(
+      ntensors, size_of, fill, nchunks, total,
+      [&](const Chunk& c, uint64_t blocks) {
+        unsigned grid = 0;
+        int r = grid_for(kernel, static_cast<uint32_t>(blocks), &grid);
+        if (r != QOPT_OK) return r;
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, c, args...);
+        return launch_status();
+      },
+      &fits);
+}
+
+// Descriptor fillers of the step and the codec.
+struct StepFill {
+  const qopt_tensor* t;
+  size_t psize, gsize;
+  bool operator()(StepChunk& c, uint32_t slot, int32_t i) const {
+    const qopt_tensor& x = t[i];
+    c.param[slot] = x.param;
+    c.grad[slot] = x.grad;
+    c.m_codes[slot] = x.m_codes;
+    c.v_codes[slot] = x.v_codes;
+    c.m_absmax[slot] = x.m_absmax;
+    c.v_absmax[slot] = x.v_absmax;
+    c.n[slot] = x.n;
+    return aligned(x.param, 4 * psize) && aligned(x.grad, 4 * gsize) && aligned(x.m_codes, 4) &&
+           aligned(x.v_codes, 4);
+  }
+};
+
+struct StepSize {
+  const qopt_tensor* t;
+  int64_t operator()(int32_t i) const { return t[i].n; }
+};
+
+struct CodecFill {
+  const qopt_codec_tensor* t;
+  bool operator()(CodecChunk& c, uint32_t slot, int32_t i) const {
+    const qopt_codec_tensor& x = t[i];
+    c.vals[slot] = x.values;
+    c.codes[slot] = x.codes;
+    c.absmax[slot] = x.absmax;
+    c.n[slot] = x.n;
+    return aligned(x.values, 16) && aligned(x.codes, 4);
+  }
+};
+
+struct CodecSize {
+  const qopt_codec_tensor* t;
+  int64_t operator()(int32_t i) const { return t[i].n; }
+};
+
 template <typename PT, typename GT>
 int launch_step_chunks(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size_t gsize,
                        const AdamScalars& k, const qopt_codebook* cbm, const qopt_codebook* cbv,
                        hipStream_t stream) {
-  auto kernel = adam8bit_kernel<PT, GT>;
-  uint64_t nchunks = 0, total = 0;
-  int rc = count_chunks(tensors, ntensors, psize, gsize, &nchunks, &total);
-  if (rc != QOPT_OK || total == 0) return rc;
-  unsigned grid = 0;
-  bool fits = true;
-  return plan_chunks(
-      tensors, ntensors, psize, gsize, nchunks, total,
-      [&](const StepChunk& c, uint64_t blocks) {
-        int r = grid_for(kernel, static_cast<uint32_t>(blocks), &grid);
-        if (r != QOPT_OK) return r;
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, c, k, cbm, cbv);
-        return launch_status();
-      },
-      &fits);
+  return launch_planned<StepChunk>(adam8bit_kernel<PT, GT>, ntensors, StepSize{tensors},
+                                   StepFill{tensors, psize, gsize}, stream, k, cbm, cbv);
 }
 
 int check_step_tensors(const qopt_tensor* tensors, int32_t ntensors, int param_dtype,
@@ -813,28 +916,58 @@ int check_step_tensors(const qopt_tensor* tensors, int32_t ntensors, int param_d
 
 // ------------------------------------------------------------ entry points
 
+namespace {
+
+int check_codec_tensors(const qopt_codec_tensor* tensors, int32_t ntensors, bool* any) {
+  if (ntensors < 0) return QOPT_EINVAL;
+  if (ntensors > 0 && tensors == nullptr) return QOPT_EINVAL;
+  *any = false;
+  for (int32_t i = 0; i < ntensors; ++i) {
+    const qopt_codec_tensor& t = tensors[i];
+    if (t.n < 0) return QOPT_EINVAL;
+    if (t.n == 0) continue;
+    *any = true;
+    if (!t.values || !t.codes || !t.absmax) return QOPT_EINVAL;
+    if (!aligned(t.values, 4) || !aligned(t.absmax, 4)) return QOPT_EALIGN;
+  }
+  return QOPT_OK;
+}
+
+template <typename Kernel>
+int codec_multi(Kernel kernel, const qopt_codebook* cb_dev, const qopt_codec_tensor* tensors,
+                int32_t ntensors, void* stream) {
+  bool any = false;
+  int rc = check_codec_tensors(tensors, ntensors, &any);
+  if (rc != QOPT_OK || !any) return rc;
+  if (!cb_dev) return QOPT_EINVAL;
+  if (!aligned(cb_dev, 16)) return QOPT_EALIGN;
+  return launch_planned<CodecChunk>(kernel, ntensors, CodecSize{tensors}, CodecFill{tensors},
+                                    static_cast<hipStream_t>(stream), cb_dev);
+}
+
+}  // namespace
+
+extern "C" int qopt_quantize_blockwise_multi(const qopt_codebook* cb_dev,
+                                             const qopt_codec_tensor* tensors, int32_t ntensors,
+                                             void* stream) {
+  return codec_multi(quantize_kernel, cb_dev, tensors, ntensors, stream);
+}
+
+extern "C" int qopt_dequantize_blockwise_multi(const qopt_codebook* cb_dev,
+                                               const qopt_codec_tensor* tensors, int32_t ntensors,
+                                               void* stream) {
+  return codec_multi(dequantize_kernel, cb_dev, tensors, ntensors, stream);
+}
+
 extern "C" int qopt_quantize_blockwise(const qopt_codebook* cb_dev, const float* x_dev, int64_t n,
                                        uint8_t* codes_dev, float* absmax_dev, void* stream) {
   if (n < 0) return QOPT_EINVAL;
   if (n == 0) return QOPT_OK;
   if (!cb_dev || !x_dev || !codes_dev || !absmax_dev) return QOPT_EINVAL;
   if (!aligned(cb_dev, 16) || !aligned(x_dev, 4) || !aligned(absmax_dev, 4)) return QOPT_EALIGN;
-  const uint64_t nb = (static_cast<uint64_t>(n) + QOPT_BLOCK - 1) / QOPT_BLOCK;
-  if (nb > 0xFFFFFFFFull) return QOPT_EINVAL;
-  CodecArgs a = {};
-  a.cb = cb_dev;
-  a.x = x_dev;
-  a.codes_out = codes_dev;
-  a.absmax_out = absmax_dev;
-  a.n = n;
-  a.nblocks = static_cast<uint32_t>(nb);
-  a.vector_ok = aligned(x_dev, 16) && aligned(codes_dev, 4);
-  unsigned grid = 0;
-  int rc = grid_for(quantize_kernel, a.nblocks, &grid);
-  if (rc != QOPT_OK) return rc;
-  hipLaunchKernelGGL(quantize_kernel, dim3(grid), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return launch_status();
+  // the kernel only reads `values` when quantizing
+  const qopt_codec_tensor t = {const_cast<float*>(x_dev), codes_dev, absmax_dev, n};
+  return codec_multi(quantize_kernel, cb_dev, &t, 1, stream);
 }
 
 extern "C" int qopt_dequantize_blockwise(const qopt_codebook* cb_dev, const uint8_t* codes_dev,
@@ -844,22 +977,10 @@ extern "C" int qopt_dequantize_blockwise(const qopt_codebook* cb_dev, const uint
   if (n == 0) return QOPT_OK;
   if (!cb_dev || !codes_dev || !absmax_dev || !y_dev) return QOPT_EINVAL;
   if (!aligned(cb_dev, 16) || !aligned(y_dev, 4) || !aligned(absmax_dev, 4)) return QOPT_EALIGN;
-  const uint64_t nb = (static_cast<uint64_t>(n) + QOPT_BLOCK - 1) / QOPT_BLOCK;
-  if (nb > 0xFFFFFFFFull) return QOPT_EINVAL;
-  CodecArgs a = {};
-  a.cb = cb_dev;
-  a.y = y_dev;
-  a.codes_in = codes_dev;
-  a.absmax_in = absmax_dev;
-  a.n = n;
-  a.nblocks = static_cast<uint32_t>(nb);
-  a.vector_ok = aligned(y_dev, 16) && aligned(codes_dev, 4);
-  unsigned grid = 0;
-  int rc = grid_for(dequantize_kernel, a.nblocks, &grid);
-  if (rc != QOPT_OK) return rc;
-  hipLaunchKernelGGL(dequantize_kernel, dim3(grid), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return launch_status();
+  // the kernel only reads `codes` and `absmax` when dequantizing
+  const qopt_codec_tensor t = {y_dev, const_cast<uint8_t*>(codes_dev),
+                               const_cast<float*>(absmax_dev), n};
+  return codec_multi(dequantize_kernel, cb_dev, &t, 1, stream);
 }
 
 extern "C" int qopt_adam8bit_step(const qopt_tensor* tensors, int32_t ntensors, int param_dtype,
@@ -908,8 +1029,10 @@ extern "C" int qopt_adam8bit_launch_count(const qopt_tensor* tensors, int32_t nt
   int rc = check_step_tensors(tensors, ntensors, param_dtype, grad_dtype, &any);
   if (rc != QOPT_OK) return rc;
   uint64_t nchunks = 0, total = 0;
-  rc = count_chunks(tensors, ntensors, param_dtype == QOPT_F32 ? 4 : 2,
-                    grad_dtype == QOPT_F32 ? 4 : 2, &nchunks, &total);
+  rc = count_chunks<StepChunk>(ntensors, StepSize{tensors},
+                               StepFill{tensors, param_dtype == QOPT_F32 ? 4u : 2u,
+                                        grad_dtype == QOPT_F32 ? 4u : 2u},
+                               &nchunks, &total);
   if (rc != QOPT_OK) return rc;
   *launches = static_cast<int64_t>(nchunks);
   return QOPT_OK;

@@ -117,6 +117,51 @@ def qopt_dequantize_blockwise(codes, absmax, kind=SIGNED, out=None):
     return out
 
 
+def _codec_array(triples):
+    """ctypes array of qopt_codec_tensor from (values, codes, absmax) triples."""
+    arr = (_lib.qopt_codec_tensor * len(triples))()
+    dev = None
+    for i, (vals, codes, absmax) in enumerate(triples):
+        n = vals.numel()
+        if vals.dtype != torch.float32 or codes.dtype != torch.uint8 or \
+                absmax.dtype != torch.float32:
+            raise TypeError("values must be float32, codes uint8, absmax float32")
+        if codes.numel() != n or absmax.numel() != nblocks(n):
+            raise ValueError("codes must hold n and absmax ceil(n / 2048) elements")
+        d = _check_cuda(vals, codes, absmax)
+        if dev is None:
+            dev = d
+        elif d != dev:
+            raise ValueError("all tensors of one call must be on the same GPU")
+        arr[i] = _lib.qopt_codec_tensor(vals.data_ptr(), codes.data_ptr(), absmax.data_ptr(), n)
+    return arr, dev
+
+
+def qopt_quantize_blockwise_multi(triples, kind=SIGNED):
+    """Quantize many fp32 tensors in few launches: ``triples`` is a list of
+    (x, codes, absmax) with preallocated uint8 codes [n] and fp32 absmax
+    [ceil(n / 2048)], written in place."""
+    arr, dev = _codec_array(triples)
+    if dev is None:
+        return
+    with torch.cuda.device(dev):
+        rc = LIB.qopt_quantize_blockwise_multi(_ptr(codebook(kind, dev)), arr, len(arr),
+                                               ctypes.c_void_p(_lib.stream_handle(dev)))
+    _lib.check("qopt_quantize_blockwise_multi", rc)
+
+
+def qopt_dequantize_blockwise_multi(triples, kind=SIGNED):
+    """Dequantize many tensors in few launches: ``triples`` is a list of
+    (y, codes, absmax) with preallocated fp32 outputs y [n], written in place."""
+    arr, dev = _codec_array(triples)
+    if dev is None:
+        return
+    with torch.cuda.device(dev):
+        rc = LIB.qopt_dequantize_blockwise_multi(_ptr(codebook(kind, dev)), arr, len(arr),
+                                                 ctypes.c_void_p(_lib.stream_handle(dev)))
+    _lib.check("qopt_dequantize_blockwise_multi", rc)
+
+
 def make_tensor_array(tensors):
     """ctypes array of qopt_tensor from tuples (param, grad, m_codes, v_codes,
     m_absmax, v_absmax); checks every tuple and returns (array, pdtype, gdtype, device)."""

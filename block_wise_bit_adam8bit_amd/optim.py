@@ -13,7 +13,9 @@ from collections import defaultdict
 
 import torch
 
+from .checkpoint import compress_moments_multi, decompress_moments_multi
 from .functional import make_tensor_array, nblocks, qopt_adam8bit_step
+
 
 class Adam8bit(torch.optim.Optimizer):
     def __init__(self, params, lr=1e-3, betas=(0.9, 0.999), eps=1e-8):
@@ -79,13 +81,7 @@ class Adam8bit(torch.optim.Optimizer):
         fp32 block maxima into parameter-typed values; this one keeps their dtypes and
         only moves them to the parameter's device."""
         saved_groups = state_dict["param_groups"]
-        if len(saved_groups) != len(self.param_groups):
-            raise ValueError("state dict has a different number of parameter groups")
-        by_id = {}
-        for group, saved in zip(self.param_groups, saved_groups):
-            if len(group["params"]) != len(saved["params"]):
-                raise ValueError("state dict has a different number of parameters in a group")
-            by_id.update(zip(saved["params"], group["params"]))
+        by_id = self._params_by_saved_id(saved_groups)
         state = defaultdict(dict)
         for pid, st in state_dict["state"].items():
             p = by_id[pid]
@@ -106,3 +102,74 @@ class Adam8bit(torch.optim.Optimizer):
                 if k != "params":
                     group[k] = v
         self._prepared = {}
+
+    def _params_by_saved_id(self, saved_groups):
+        if len(saved_groups) != len(self.param_groups):
+            raise ValueError("state dict has a different number of parameter groups")
+        by_id = {}
+        for group, saved in zip(self.param_groups, saved_groups):
+            if len(group["params"]) != len(saved["params"]):
+                raise ValueError("state dict has a different number of parameters in a group")
+            by_id.update(zip(saved["params"], group["params"]))
+        return by_id
+
+    @torch.no_grad()
+    def load_fp32_adam_state(self, adam_state_dict):
+        """Take over the state of a ``torch.optim.Adam`` state dict with the same
+        parameter groups: each parameter's fp32 ``exp_avg`` / ``exp_avg_sq`` are
+        quantized block-wise into this optimizer's 8-bit state (the moment codec of
+        ``checkpoint.py``), its step count is kept, and lr, betas and eps are taken
+        from the Adam groups.  Adam with weight decay or amsgrad has no 8-bit
+        equivalent here and is refused."""
+        saved_groups = adam_state_dict["param_groups"]
+        for g in saved_groups:
+            if g.get("amsgrad", False) or g.get("weight_decay", 0.0) != 0.0:
+                raise ValueError("only plain Adam (no amsgrad, no weight decay) converts")
+        by_id = self._params_by_saved_id(saved_groups)
+        state = defaultdict(dict)
+        by_device = defaultdict(list)
+        for pid, st in adam_state_dict["state"].items():
+            p = by_id[pid]
+            if st["exp_avg"].numel() != p.numel():
+                raise ValueError("moment size differs from its parameter")
+            by_device[p.device].append((p, st))
+        for dev, items in by_device.items():
+            codes = compress_moments_multi([(st["exp_avg"].to(dev), st["exp_avg_sq"].to(dev))
+                                            for _, st in items])
+            for (p, st), new in zip(items, codes):
+                step = st["step"]
+                new["step"] = int(step.item() if torch.is_tensor(step) else step)
+                state[p] = new
+        self.state = state
+        for group, saved in zip(self.param_groups, saved_groups):
+            group["lr"] = saved["lr"]
+            group["betas"] = tuple(saved["betas"])
+            group["eps"] = saved["eps"]
+        self._prepared = {}
+
+    @torch.no_grad()
+    def fp32_adam_state_dict(self):
+        """A ``torch.optim.Adam``-loadable state dict: the moments dequantized to
+        fp32 in each parameter's shape, the step as a float tensor, plain-Adam group
+        settings.  (``torch.optim.Adam.load_state_dict`` casts the moments to the
+        parameter dtype.)"""
+        sd = self.state_dict()
+        out_state = {}
+        params = [p for g in self.param_groups for p in g["params"]]
+        by_device = defaultdict(list)
+        for pid, st in sd["state"].items():
+            by_device[st["m_codes"].device].append((pid, st))
+        for items in by_device.values():
+            moments = decompress_moments_multi([st for _, st in items],
+                                               shapes=[params[pid].shape for pid, _ in items])
+            for (pid, st), (m, v) in zip(items, moments):
+                out_state[pid] = {"step": torch.tensor(float(st["step"])), "exp_avg": m,
+                                  "exp_avg_sq": v}
+        adam_defaults = torch.optim.Adam([torch.zeros(1)]).defaults  # this torch's keys
+        groups = []
+        for g in sd["param_groups"]:
+            ng = dict(adam_defaults)
+            ng.update(lr=g["lr"], betas=tuple(g["betas"]), eps=g["eps"], weight_decay=0.0,
+                      amsgrad=False, params=list(g["params"]))
+            groups.append(ng)
+        return {"state": out_state, "param_groups": groups}

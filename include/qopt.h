@@ -134,6 +134,38 @@ int qopt_dequantize_blockwise(const qopt_codebook* cb_dev, const uint8_t* codes_
                               void* stream);
 
 /*
+ * One tensor of a multi-tensor codec call.  All pointers are device memory:
+ *   values  n fp32 values (read when quantizing, written when dequantizing),
+ *           4-byte aligned;
+ *   codes   n code bytes (written when quantizing, read when dequantizing);
+ *   absmax  ceil(n / 2048) fp32 block maxima, 4-byte aligned.
+ * Blocks restart at element 0 of every tensor.  Tensors whose values are 16-byte
+ * aligned and whose codes are 4-byte aligned take the vector path.
+ */
+typedef struct qopt_codec_tensor {
+  float* values;
+  uint8_t* codes;
+  float* absmax;
+  int64_t n;
+} qopt_codec_tensor;
+
+/*
+ * Multi-tensor forms of qopt_quantize_blockwise / qopt_dequantize_blockwise: the same
+ * per-block results for every tensor of the host array `tensors`, in launches of equal
+ * block counts with at most 48 tensor pieces each (as for qopt_adam8bit_step) instead
+ * of one launch per tensor.  This is the moment codec of optimizer checkpoints (the
+ * checkpoint-compression page, ExCP: momentum stored as a codebook plus per-element
+ * indices).  Checks: tensors != NULL when ntensors > 0, ntensors >= 0, every n >= 0,
+ * non-null pointers for n > 0, alignment as above; tensors with n == 0 are skipped.
+ * No tensor may overlap another's buffers.
+ */
+int qopt_quantize_blockwise_multi(const qopt_codebook* cb_dev, const qopt_codec_tensor* tensors,
+                                  int32_t ntensors, void* stream);
+int qopt_dequantize_blockwise_multi(const qopt_codebook* cb_dev,
+                                    const qopt_codec_tensor* tensors, int32_t ntensors,
+                                    void* stream);
+
+/*
  * One parameter tensor of an 8-bit Adam step.  All pointers are device memory:
  *   param    n elements of the step's param dtype, updated in place;
  *   grad     n elements of the step's grad dtype, read only;

@@ -181,3 +181,25 @@ def test_launch_plan_host_only(shapes, want):
     assert qopt.LIB.qopt_adam8bit_launch_count(many, 1000, 0, 0, ctypes.byref(out)) == 0
     assert out.value == 21
     assert qopt.LIB.qopt_adam8bit_launch_count(arr, 1, 0, 0, None) == qopt.QOPT_EINVAL
+
+
+def test_multi_codec_argument_checks():
+    L = qopt.LIB
+    C = _lib.qopt_codec_tensor
+    null = ctypes.c_void_p(0)
+    p = ctypes.c_void_p(0x1000)
+    for fn in (L.qopt_quantize_blockwise_multi, L.qopt_dequantize_blockwise_multi):
+        assert fn(null, None, 0, null) == qopt.QOPT_OK
+        assert fn(null, None, 2, null) == qopt.QOPT_EINVAL
+        ok = (C * 1)(C(0x1000, 0x2000, 0x3000, 10))
+        assert fn(p, ok, -1, null) == qopt.QOPT_EINVAL
+        empty = (C * 2)(C(0, 0, 0, 0), C(0, 0, 0, 0))
+        assert fn(null, empty, 2, null) == qopt.QOPT_OK          # nothing to do
+        assert fn(null, ok, 1, null) == qopt.QOPT_EINVAL         # no codebook
+        assert fn(ctypes.c_void_p(0x1008), ok, 1, null) == qopt.QOPT_EALIGN
+        neg = (C * 1)(C(0x1000, 0x2000, 0x3000, -1))
+        assert fn(p, neg, 1, null) == qopt.QOPT_EINVAL
+        nul = (C * 1)(C(0x1000, 0, 0x3000, 10))
+        assert fn(p, nul, 1, null) == qopt.QOPT_EINVAL
+        mis = (C * 1)(C(0x1002, 0x2000, 0x3000, 10))
+        assert fn(p, mis, 1, null) == qopt.QOPT_EALIGN
