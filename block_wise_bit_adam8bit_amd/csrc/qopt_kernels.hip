@@ -25,6 +25,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <type_traits>
 
 #include "qopt.h"
 
@@ -48,20 +49,22 @@ static_assert(kSlices * kWave * 4 == QOPT_BLOCK, "block layout");
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Cache policy per stream, chosen by measurement on MI355X: the wide streams
-// (parameters, gradients, codec values) go non-temporal; the one-byte code streams
-// use ordinary cached accesses.
+// Cache policy per stream, chosen by measurement on MI355X (each choice compared
+// with the others in one process, on the same buffers): the wide streams
+// (parameters, gradients, codec values) go non-temporal, and so do the step's
+// one-byte code streams; the codec's code streams use ordinary cached accesses
+// (non-temporal ones measured 5-17 % slower there, while the step gains about 0.5 %).
 #ifndef QOPT_NT_WIDE_LOAD
 #define QOPT_NT_WIDE_LOAD 1
 #endif
 #ifndef QOPT_NT_WIDE_STORE
 #define QOPT_NT_WIDE_STORE 1
 #endif
-#ifndef QOPT_NT_CODE_LOAD
-#define QOPT_NT_CODE_LOAD 0
+#ifndef QOPT_NT_STEP_CODES
+#define QOPT_NT_STEP_CODES 1
 #endif
-#ifndef QOPT_NT_CODE_STORE
-#define QOPT_NT_CODE_STORE 0
+#ifndef QOPT_NT_CODEC_CODES
+#define QOPT_NT_CODEC_CODES 0
 #endif
 
 template <bool kNt, typename T>
@@ -80,11 +83,17 @@ template <typename T> __device__ __forceinline__ T ld_wide(const T* p) {
 template <typename T> __device__ __forceinline__ void st_wide(T* p, T v) {
   st_policy<QOPT_NT_WIDE_STORE != 0>(p, v);
 }
-template <typename T> __device__ __forceinline__ T ld_code(const T* p) {
-  return ld_policy<QOPT_NT_CODE_LOAD != 0>(p);
+template <typename T> __device__ __forceinline__ T ld_step_code(const T* p) {
+  return ld_policy<QOPT_NT_STEP_CODES != 0>(p);
 }
-template <typename T> __device__ __forceinline__ void st_code(T* p, T v) {
-  st_policy<QOPT_NT_CODE_STORE != 0>(p, v);
+template <typename T> __device__ __forceinline__ void st_step_code(T* p, T v) {
+  st_policy<QOPT_NT_STEP_CODES != 0>(p, v);
+}
+template <typename T> __device__ __forceinline__ T ld_codec_code(const T* p) {
+  return ld_policy<QOPT_NT_CODEC_CODES != 0>(p);
+}
+template <typename T> __device__ __forceinline__ void st_codec_code(T* p, T v) {
+  st_policy<QOPT_NT_CODEC_CODES != 0>(p, v);
 }
 
 // ------------------------------------------------------------------ helpers
@@ -309,7 +318,7 @@ quantize_kernel(CodecChunk c, const qopt_codebook* cb_g) {
         uint32_t w = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) w |= encode_signed(enc, sc, x[s][j]) << (8 * j);
-        st_code(dst + s * kWave + lane, w);
+        st_codec_code(dst + s * kWave + lane, w);
       }
     } else {
 #pragma unroll
@@ -350,7 +359,7 @@ dequantize_kernel(CodecChunk c, const qopt_codebook* cb_g) {
       f32x4* dst = reinterpret_cast<f32x4*>(r.vals + r.base);
       uint32_t w[kSlices];
 #pragma unroll
-      for (int s = 0; s < kSlices; ++s) w[s] = ld_code(src + s * kWave + lane);
+      for (int s = 0; s < kSlices; ++s) w[s] = ld_codec_code(src + s * kWave + lane);
 #pragma unroll
       for (int s = 0; s < kSlices; ++s) {
         f32x4 v;
@@ -376,6 +385,7 @@ dequantize_kernel(CodecChunk c, const qopt_codebook* cb_g) {
 
 struct AdamScalars {
   float b1, b2, omb1, omb2, eps, step_size, inv_sqrt_bc2;
+  uint32_t bf16_screen;  // 1: bf16 parameters may take the screened short path
 };
 
 // One launch's work: up to kMaxTensors pieces, each a run of whole blocks of one
@@ -459,6 +469,28 @@ __device__ __forceinline__ float sqrt_rn_unscaled(float x) {
 
 constexpr float kTinyMoment = 0x1p-96f;  // below this, sqrt_rn_unscaled is not exact
 
+// Screen for the bf16 short path.  pf = p - t was computed with a square root and a
+// reciprocal that are each within one ulp (v >= 2^-96 and a normal or zero
+// denominator: every such input was checked on the hardware).  Against the
+// correctly rounded sequence, the relative error of the quotient is below 2^-20.7,
+// so the exact p - t lies within |t| 2^-20 + |pf| 2^-24 of pf (plus 2^-149 where
+// results are subnormal).  c doubles that bound and adds 2^-126; every x in
+// [pf - c, pf + c] therefore covers the exact value, and rounding fp32 -> bf16 is
+// monotone, so if both ends give the same bf16 bits so do the exact value and pf.
+__device__ __forceinline__ float screen_width(float pf, float t) {
+  return __builtin_fmaf(fabsf(t), 0x1p-18f, __builtin_fmaf(fabsf(pf), 0x1p-20f, 0x1p-126f));
+}
+// Two elements at once: the bf16 bits of both lower ends against both upper ends.
+// A NaN result (0/0 with eps = 0) fails through the unordered test; an infinite
+// one makes one end NaN and the other infinite, which differ.
+__device__ __forceinline__ uint32_t screen_bf16x2(float pf0, float t0, float pf1, float t1) {
+  const float c0 = screen_width(pf0, t0);
+  const float c1 = screen_width(pf1, t1);
+  const uint32_t lo = pack_bf16x2(pf0 - c0, pf1 - c1);
+  const uint32_t hi = pack_bf16x2(pf0 + c0, pf1 + c1);
+  return (lo ^ hi) | static_cast<uint32_t>(__builtin_isunordered(pf0, pf1));
+}
+
 // Where one block lives, resolved from the launch's piece table (wave-uniform).
 struct BlockRef {
   void* param;
@@ -518,8 +550,8 @@ __device__ __forceinline__ void load_block(BlockIn<PT, GT>& in, const BlockRef& 
     const int idx = s * kWave + lane;
     in.p[s] = ld_wide(p + idx);
     in.g[s] = ld_wide(g + idx);
-    in.cm[s] = ld_code(cm + idx);
-    in.cv[s] = ld_code(cv + idx);
+    in.cm[s] = ld_step_code(cm + idx);
+    in.cv[s] = ld_step_code(cv + idx);
   }
 }
 
@@ -538,7 +570,6 @@ __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_code
     unpack4(in.g[s], g4);
     // the moments of the slice's 4 elements, then their square roots: the short
     // sequence unless some lane of the wave holds a tiny second moment
-    float sq[4];
     uint64_t tiny = 0;  // lanes (as a wave mask) holding 0 < v < 2^-96
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -550,18 +581,49 @@ __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_code
       tiny |= __builtin_amdgcn_ballot_w64((__float_as_uint(v[s][j]) - 1u) <
                                           (__float_as_uint(kTinyMoment) - 1u));
     }
-    if (tiny != 0) {
+    bool exact = true;
+    if constexpr (std::is_same<PT, uint16_t>::value) {
+      // bf16 parameters: the short path (hardware square root and reciprocal, each
+      // within one ulp on the inputs that reach it) gives the same bf16 result as
+      // the correctly rounded sequence whenever its fp32 result is far enough from
+      // a bf16 rounding boundary; lanes where it is not fall back below.
+      if (tiny == 0 && k.bf16_screen) {
+        float pf[4], t[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sq[j] = sqrtf(v[s][j]);
-    } else {
+        for (int j = 0; j < 4; ++j) {
+          const float sq1 = __builtin_amdgcn_sqrtf(v[s][j]);
+          const float denom = (sq1 * k.inv_sqrt_bc2) + k.eps;
+          const float u = m[s][j] * __builtin_amdgcn_rcpf(denom);
+          t[j] = k.step_size * u;
+          pf[j] = p4[j] - t[j];
+        }
+        const uint32_t unsafe = screen_bf16x2(pf[0], t[0], pf[1], t[1]) |
+                                screen_bf16x2(pf[2], t[2], pf[3], t[3]);
+        if (__builtin_amdgcn_ballot_w64(unsafe != 0) == 0) {
+          exact = false;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sq[j] = sqrt_rn_unscaled(v[s][j]);
+          for (int j = 0; j < 4; ++j) p4[j] = pf[j];
+        }
+      }
+    }
+    if (exact) {
+      float sq[4];
+      if (tiny != 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sq[j] = sqrtf(v[s][j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sq[j] = sqrt_rn_unscaled(v[s][j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float denom = (sq[j] * k.inv_sqrt_bc2) + k.eps;
+        const float u = m[s][j] / denom;
+        p4[j] = p4[j] - (k.step_size * u);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float denom = (sq[j] * k.inv_sqrt_bc2) + k.eps;
-      const float u = m[s][j] / denom;
-      p4[j] = p4[j] - (k.step_size * u);
       mmax = fmaxf(mmax, fabsf(m[s][j]));
       vmax = fmaxf(vmax, v[s][j]);
     }
@@ -618,8 +680,8 @@ __device__ __forceinline__ void requantize(const Encoder& em, const Encoder& ev,
       wv |= encode_nonneg(ev, sv, v[s][j]) << (8 * j);
     }
     if (r.vec) {
-      st_code(cmo + s * kWave + lane, wm);
-      st_code(cvo + s * kWave + lane, wv);
+      st_step_code(cmo + s * kWave + lane, wm);
+      st_step_code(cvo + s * kWave + lane, wv);
       } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1011,6 +1073,12 @@ extern "C" int qopt_adam8bit_step(const qopt_tensor* tensors, int32_t ntensors, 
   const double bc2 = 1.0 - pow_by_squaring(static_cast<double>(hp->beta2), hp->step);
   k.step_size = static_cast<float>(static_cast<double>(hp->lr) / bc1);
   k.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
+  // The screen's error bound needs a normal (or zero) denominator in front of the
+  // hardware reciprocal, whose accuracy was only established on normal inputs, so
+  // no subnormal eps; and a step size below 2^20, so that subnormal rounding errors
+  // scaled by it stay under the bound's 2^-126 floor.
+  k.bf16_screen =
+      ((hp->eps == 0.0f || hp->eps >= 0x1p-126f) && k.step_size <= 0x1p20f) ? 1u : 0u;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (param_dtype == QOPT_F32 && grad_dtype == QOPT_F32)

@@ -208,6 +208,22 @@ def test_tiny_second_moments(q, pdt, gdt):
     run_small(q, [4 * 2048 + 77], pdt, gdt, steps=3, seed=11, grads=grads)
 
 
+@pytest.mark.parametrize("gdt", ["bf16", "f32"])
+@pytest.mark.parametrize("hp", [HP,
+                                dict(lr=5e-2, beta1=0.5, beta2=0.75, eps=1e-6),
+                                dict(lr=1e-4, beta1=0.95, beta2=0.9999, eps=0.0),
+                                dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-40),
+                                dict(lr=4e6, beta1=0.9, beta2=0.999, eps=1e-8)])
+def test_bf16_params_short_path(q, hp, gdt):
+    """bf16 parameters over 2^19 + 333 elements: the kernel's short path for bf16
+    results (hardware square root and reciprocal behind an error screen) must give
+    the oracle's bf16 bits everywhere.  lr = 5e-2 puts many updates next to the
+    parameter's own size, so many slices fail the screen and take the correctly
+    rounded path; a subnormal eps and a step size above 2^20 switch the screen off."""
+    say(f"bf16 short path {hp} grads {gdt}")
+    run_small(q, [2 ** 19 + 333], "bf16", gdt, steps=3, seed=12, hp=hp)
+
+
 def test_late_step_and_zero_blocks(q):
     """A large step number, and blocks whose gradient and state are zero."""
     n = 4 * 2048
