@@ -24,6 +24,10 @@ Where the page is silent, the readings are fixed here and listed in each module'
 docstring.  Parity status of every function is stated in its docstring: "pinned"
 means a ``-m "not gpu"`` test checks it against something other than itself.
 
+The Stable Embedding layer of the same page (§2 "Stable Embedding Layer") has its
+own module, ``oracle.embedding``: Xavier-uniform initialisation from a counter-based
+generator, and LayerNorm after the lookup, forward and backward, in binary64.
+
 Arithmetic precision: the codes are integers decided by fp32 arithmetic, so every
 step that feeds a code decision (the moments, the block absmax, the normalisation)
 is evaluated in IEEE binary32, one rounding per operation, in the order written in
