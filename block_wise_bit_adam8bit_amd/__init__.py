@@ -1,7 +1,8 @@
 """block_wise_bit_adam8bit_amd: block-wise dynamic-tree 8-bit Adam for MI355X.
 
 The compute lives in libqopt.so (HIP kernels for gfx950 behind the C ABI of
-include/qopt.h); this package is its thin Python binding plus a torch optimizer.
+include/qopt.h, include/qopt_embedding.h); this package is its thin Python binding
+plus a torch optimizer and the Stable Embedding module.
 Importing it loads the library and fails with ImportError if it is not built.
 """
 
@@ -20,5 +21,9 @@ from .checkpoint import (  # noqa: F401
     compress_moments, decompress_moments, compress_moments_multi, decompress_moments_multi,
 )
 from .optim import Adam8bit  # noqa: F401
+from .embedding import (  # noqa: F401
+    StableEmbedding, StableEmbeddingFunction, qopt_embedding_xavier_init,
+    qopt_stable_embedding_forward, qopt_stable_embedding_backward,
+)
 
 __version__ = "0.1.0"

@@ -15,6 +15,7 @@ import torch  # noqa: F401  (must be loaded before libqopt.so; see module docstr
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqopt.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "qopt.h")
+EMB_HEADER = os.path.join(os.path.dirname(_HERE), "include", "qopt_embedding.h")
 
 QOPT_BLOCK = 2048
 QOPT_OK, QOPT_EINVAL, QOPT_EUNSUPPORTED, QOPT_EALIGN, QOPT_ELAUNCH, QOPT_EINTERNAL = range(6)
@@ -23,6 +24,7 @@ QOPT_F32, QOPT_BF16 = 0, 1
 QOPT_CODEBOOK_MAGIC = 0x31424351
 QOPT_MAX_BUCKETS = 7168
 QOPT_THRESH_LEN = 272
+QOPT_EMB_VEC_MAX_DIM = 4096
 
 
 class QoptError(RuntimeError):
@@ -97,6 +99,27 @@ _SIGNATURES = {
     "qopt_adam8bit_launch_count": (ctypes.c_int, [ctypes.POINTER(qopt_tensor), ctypes.c_int32,
                                                   ctypes.c_int, ctypes.c_int,
                                                   ctypes.POINTER(ctypes.c_int64)]),
+    "qopt_embedding_xavier_init": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                                  ctypes.c_int64, ctypes.c_uint64,
+                                                  ctypes.c_void_p]),
+    "qopt_stable_embedding_forward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                                     ctypes.c_int64, ctypes.c_void_p,
+                                                     ctypes.c_int64, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_float,
+                                                     ctypes.c_void_p, ctypes.c_int,
+                                                     ctypes.c_void_p, ctypes.c_void_p,
+                                                     ctypes.c_void_p, ctypes.c_void_p]),
+    "qopt_stable_embedding_backward_workspace": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64,
+                                                                ctypes.POINTER(ctypes.c_size_t)]),
+    "qopt_stable_embedding_backward": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
+                                                      ctypes.c_int64, ctypes.c_int64,
+                                                      ctypes.c_void_p, ctypes.c_int64,
+                                                      ctypes.c_void_p, ctypes.c_void_p,
+                                                      ctypes.c_void_p, ctypes.c_void_p,
+                                                      ctypes.c_int, ctypes.c_void_p,
+                                                      ctypes.c_void_p, ctypes.c_void_p,
+                                                      ctypes.c_void_p, ctypes.c_size_t,
+                                                      ctypes.c_void_p]),
     "qopt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qopt_version": (ctypes.c_int, []),
 }
@@ -118,11 +141,12 @@ def _load():
 LIB = _load()
 
 
-def header_constants(path=HEADER):
-    """#define values of include/qopt.h (used by tests to check this mirror)."""
+def header_constants(paths=(HEADER, EMB_HEADER)):
+    """#define values of include/*.h (used by tests to check this mirror)."""
     out = {}
-    for m in re.finditer(r"#define\s+(QOPT_\w+)\s+(0x[0-9a-fA-F]+|\d+)u?", open(path).read()):
-        out[m.group(1)] = int(m.group(2), 0)
+    for path in paths:
+        for m in re.finditer(r"#define\s+(QOPT_\w+)\s+(0x[0-9a-fA-F]+|\d+)u?", open(path).read()):
+            out[m.group(1)] = int(m.group(2), 0)
     return out
 
 

@@ -52,14 +52,17 @@ def build(verbose=False, save_temps=False, extra_defines=()):
     os.makedirs(BUILD, exist_ok=True)
     defs = [f"-D{d}" for d in extra_defines]
     host_obj = os.path.join(BUILD, "codebook.o")
-    dev_obj = os.path.join(BUILD, "qopt_kernels.o")
     _run([hipcc, "-x", "c++", *COMMON, *defs, "-c", os.path.join(CSRC, "codebook.cpp"),
           "-o", host_obj], verbose)
     temps = ["-save-temps=obj"] if save_temps else []
-    _run([hipcc, "-x", "hip", *COMMON, *DEVICE, *defs, *temps, "-c",
-          os.path.join(CSRC, "qopt_kernels.hip"), "-o", dev_obj], verbose)
+    dev_objs = []
+    for src in sorted(f for f in os.listdir(CSRC) if f.endswith(".hip")):
+        obj = os.path.join(BUILD, src[:-4] + ".o")
+        _run([hipcc, "-x", "hip", *COMMON, *DEVICE, *defs, *temps, "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
+        dev_objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", host_obj, dev_obj, "-o", tmp], verbose)
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", host_obj, *dev_objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

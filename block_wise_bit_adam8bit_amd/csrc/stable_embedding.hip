@@ -1,0 +1,723 @@
+// Stable Embedding layer kernels for gfx950 (include/qopt_embedding.h).
+//
+// 8-bit optimizers summary page (wiki.neutronadmin.com/news/16836), §2 "Stable
+// Embedding Layer": Xavier-uniform initialisation of the table and a layer
+// normalisation after the lookup.  YaLM-100B training page (golden-irbis.ru),
+// "Stabilizations. LayerNorm" / "Stabilizations. BFloat 16": LayerNorm right after
+// the embedding, computed in fp32.
+//
+// Execution model:
+//   - One wavefront per token row.  For rows of up to 4096 elements whose width is
+//     a multiple of 4 (the vector path), lane l holds columns s*256 + 4l .. +3 for
+//     slices s < S, in registers; row sums are a per-lane sum in slice order followed
+//     by a butterfly over the 64 lanes (every lane ends with the same bits).
+//   - Persistent workgroups walk tokens with a grid stride; gamma and beta are
+//     staged in LDS once per workgroup.
+//   - Backward: the table gradient is scattered with float atomics (rows shared by
+//     several tokens add up in arrival order); gamma and beta gradients are kept per
+//     lane in registers over a wave's tokens, combined across the workgroup's waves
+//     in wave order through LDS, written to a workspace slot per workgroup, and
+//     summed over slots in slot order by a second kernel, so they are reproducible.
+//   - Every other shape runs element-wise kernels (one wave per workgroup, columns
+//     lane, lane + 64, ...) with the same operations.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "qopt_embedding.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kVecWaves = 4;  // waves per workgroup in the vector kernels
+constexpr int kVecThreads = kWave * kVecWaves;
+constexpr int kMaxSlices = QOPT_EMB_VEC_MAX_DIM / 256;
+constexpr int kBwdSlotsPerCu = 2;  // backward workgroups (gradient slots) per CU
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// --------------------------------------------------------------- element access
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 pair -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void store(float* p, int64_t i, float x) { p[i] = x; }
+  static __device__ __forceinline__ f32x4 load4(const float* p, int64_t i) {
+    return *reinterpret_cast<const f32x4*>(p + i);
+  }
+  static __device__ __forceinline__ void store4(float* p, int64_t i, f32x4 v) {
+    *reinterpret_cast<f32x4*>(p + i) = v;
+  }
+};
+template <> struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) {
+    return bf16_bits_to_f32(p[i]);
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, int64_t i, float x) {
+    p[i] = static_cast<uint16_t>(f32x2_to_bf16x2(x, 0.0f) & 0xFFFFu);
+  }
+  static __device__ __forceinline__ f32x4 load4(const uint16_t* p, int64_t i) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(p + i);
+    return f32x4{bf16_bits_to_f32(w.x & 0xFFFFu), bf16_bits_to_f32(w.x >> 16),
+                 bf16_bits_to_f32(w.y & 0xFFFFu), bf16_bits_to_f32(w.y >> 16)};
+  }
+  static __device__ __forceinline__ void store4(uint16_t* p, int64_t i, f32x4 v) {
+    u32x2 w;
+    w.x = f32x2_to_bf16x2(v.x, v.y);
+    w.y = f32x2_to_bf16x2(v.z, v.w);
+    *reinterpret_cast<u32x2*>(p + i) = w;
+  }
+};
+
+// Sum over the 64 lanes; addition is commutative, so every lane gets the same bits.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) x = x + __shfl_xor(x, off, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float quiet_nan() { return __uint_as_float(0x7FC00000u); }
+
+// ------------------------------------------------------------------ Philox4x32-10
+// Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC 2011): ten rounds; each multiplies words 0 and 2 by two constants, mixes the
+// high halves with the other words and the key, and the key advances by two Weyl
+// constants between rounds.
+
+struct Words4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Words4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+  constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint32_t hi0 = __umulhi(kM0, c0), lo0 = kM0 * c0;
+    const uint32_t hi1 = __umulhi(kM1, c2), lo1 = kM1 * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return Words4{{c0, c1, c2, c3}};
+}
+
+// -------------------------------------------------------------------- kernels
+
+// Xavier uniform: thread i fills elements 4i .. 4i+3 from counter block i.
+template <typename WT>
+__global__ void __launch_bounds__(256) xavier_kernel(WT* w, uint64_t n, uint64_t nblocks,
+                                                     uint32_t k0, uint32_t k1, float a) {
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * blockDim.x;
+  for (uint64_t b = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x; b < nblocks;
+       b += stride) {
+    const Words4 r = philox4x32_10(static_cast<uint32_t>(b), static_cast<uint32_t>(b >> 32), 0u,
+                                   0u, k0, k1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint64_t e = 4 * b + j;
+      if (e < n) {
+        const float u = static_cast<float>(r.w[j] >> 8) * 0x1p-24f;  // exact
+        const float two_u_minus_1 = (2.0f * u) - 1.0f;                 // exact
+        Elem<WT>::store(w, static_cast<int64_t>(e), a * two_u_minus_1);
+      }
+    }
+  }
+}
+
+// Stage `dim` floats of src into LDS as S*64 float4 (zeros past dim).
+template <int S>
+__device__ __forceinline__ void stage4(f32x4* dst, const float* src, int32_t dim) {
+  for (int i = threadIdx.x; i < S * kWave; i += blockDim.x) {
+    f32x4 v;
+    const int c = 4 * i;
+    v.x = c + 0 < dim ? src[c + 0] : 0.0f;
+    v.y = c + 1 < dim ? src[c + 1] : 0.0f;
+    v.z = c + 2 < dim ? src[c + 2] : 0.0f;
+    v.w = c + 3 < dim ? src[c + 3] : 0.0f;
+    dst[i] = v;
+  }
+}
+
+template <int S, typename WT, typename OT>
+__global__ void __launch_bounds__(kVecThreads)
+fwd_vec_kernel(const WT* __restrict__ w, int64_t rows, int32_t dim, const int64_t* __restrict__ idx,
+               int64_t ntok, const float* __restrict__ gamma, const float* __restrict__ beta,
+               float eps, OT* __restrict__ out, float* __restrict__ mean_out,
+               float* __restrict__ rstd_out, int32_t* __restrict__ bad) {
+  extern __shared__ f32x4 lds4[];
+  f32x4* gam = lds4;
+  f32x4* bet = lds4 + S * kWave;
+  stage4<S>(gam, gamma, dim);
+  stage4<S>(bet, beta, dim);
+  __syncthreads();
+  const int lane = threadIdx.x % kWave;
+  const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kVecWaves;
+  const float n_dim = static_cast<float>(dim);
+  for (int64_t t = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave; t < ntok; t += stride) {
+    const int64_t r = idx[t];
+    OT* orow = out + t * dim;
+    if (r < 0 || r >= rows) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int c = s * 256 + 4 * lane;
+        if (c < dim) Elem<OT>::store4(orow, c, f32x4{quiet_nan(), quiet_nan(), quiet_nan(), quiet_nan()});
+      }
+      if (lane == 0) {
+        if (mean_out) {
+          mean_out[t] = quiet_nan();
+          rstd_out[t] = quiet_nan();
+        }
+        if (bad) atomicAdd(bad, 1);
+      }
+      continue;
+    }
+    const WT* row = w + r * dim;
+    f32x4 x[S];
+    float sum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int c = s * 256 + 4 * lane;
+      x[s] = c < dim ? Elem<WT>::load4(row, c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      sum = sum + x[s].x;
+      sum = sum + x[s].y;
+      sum = sum + x[s].z;
+      sum = sum + x[s].w;
+    }
+    const float mean = wave_sum(sum) / n_dim;
+    float sq = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int c = s * 256 + 4 * lane;
+      if (c < dim) {
+        const float d0 = x[s].x - mean, d1 = x[s].y - mean, d2 = x[s].z - mean, d3 = x[s].w - mean;
+        sq = sq + (d0 * d0);
+        sq = sq + (d1 * d1);
+        sq = sq + (d2 * d2);
+        sq = sq + (d3 * d3);
+      }
+    }
+    const float var = wave_sum(sq) / n_dim;
+    const float rstd = 1.0f / sqrtf(var + eps);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int c = s * 256 + 4 * lane;
+      if (c < dim) {
+        const f32x4 g = gam[s * kWave + lane], b = bet[s * kWave + lane];
+        f32x4 y;
+        y.x = (((x[s].x - mean) * rstd) * g.x) + b.x;
+        y.y = (((x[s].y - mean) * rstd) * g.y) + b.y;
+        y.z = (((x[s].z - mean) * rstd) * g.z) + b.z;
+        y.w = (((x[s].w - mean) * rstd) * g.w) + b.w;
+        Elem<OT>::store4(orow, c, y);
+      }
+    }
+    if (lane == 0 && mean_out) {
+      mean_out[t] = mean;
+      rstd_out[t] = rstd;
+    }
+  }
+}
+
+// Element-wise forward: one wave per workgroup, any width and alignment.
+template <typename WT, typename OT>
+__global__ void __launch_bounds__(kWave)
+fwd_elem_kernel(const WT* __restrict__ w, int64_t rows, int64_t dim, const int64_t* __restrict__ idx,
+                int64_t ntok, const float* __restrict__ gamma, const float* __restrict__ beta,
+                float eps, OT* __restrict__ out, float* __restrict__ mean_out,
+                float* __restrict__ rstd_out, int32_t* __restrict__ bad) {
+  const int lane = threadIdx.x;
+  const float n_dim = static_cast<float>(dim);
+  for (int64_t t = blockIdx.x; t < ntok; t += gridDim.x) {
+    const int64_t r = idx[t];
+    OT* orow = out + t * dim;
+    if (r < 0 || r >= rows) {
+      for (int64_t c = lane; c < dim; c += kWave) Elem<OT>::store(orow, c, quiet_nan());
+      if (lane == 0) {
+        if (mean_out) {
+          mean_out[t] = quiet_nan();
+          rstd_out[t] = quiet_nan();
+        }
+        if (bad) atomicAdd(bad, 1);
+      }
+      continue;
+    }
+    const WT* row = w + r * dim;
+    float sum = 0.0f;
+    for (int64_t c = lane; c < dim; c += kWave) sum = sum + Elem<WT>::load(row, c);
+    const float mean = wave_sum(sum) / n_dim;
+    float sq = 0.0f;
+    for (int64_t c = lane; c < dim; c += kWave) {
+      const float d = Elem<WT>::load(row, c) - mean;
+      sq = sq + (d * d);
+    }
+    const float var = wave_sum(sq) / n_dim;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    for (int64_t c = lane; c < dim; c += kWave)
+      Elem<OT>::store(orow, c, (((Elem<WT>::load(row, c) - mean) * rstd) * gamma[c]) + beta[c]);
+    if (lane == 0 && mean_out) {
+      mean_out[t] = mean;
+      rstd_out[t] = rstd;
+    }
+  }
+}
+
+__device__ __forceinline__ void atomic_add4(float* p, f32x4 v) {
+  unsafeAtomicAdd(p + 0, v.x);
+  unsafeAtomicAdd(p + 1, v.y);
+  unsafeAtomicAdd(p + 2, v.z);
+  unsafeAtomicAdd(p + 3, v.w);
+}
+
+template <int S, typename WT, typename OT>
+__global__ void __launch_bounds__(kVecThreads)
+bwd_vec_kernel(const WT* __restrict__ w, int64_t rows, int32_t dim, const int64_t* __restrict__ idx,
+               int64_t ntok, const float* __restrict__ gamma, const float* __restrict__ mean,
+               const float* __restrict__ rstd, const OT* __restrict__ dout,
+               float* __restrict__ dweight, float* __restrict__ ws) {
+  extern __shared__ f32x4 lds4[];
+  f32x4* gam = lds4;
+  f32x4* comb_g = lds4 + S * kWave;
+  f32x4* comb_b = lds4 + 2 * S * kWave;
+  stage4<S>(gam, gamma, dim);
+  __syncthreads();
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kVecWaves;
+  const float n_dim = static_cast<float>(dim);
+  f32x4 dg[S], db[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    dg[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    db[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  for (int64_t t = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave; t < ntok; t += stride) {
+    const int64_t r = idx[t];
+    if (r < 0 || r >= rows) continue;
+    const WT* row = w + r * dim;
+    const OT* dyrow = dout + t * dim;
+    const float mu = mean[t], rs = rstd[t];
+    float c1 = 0.0f, c2 = 0.0f;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int c = s * 256 + 4 * lane;
+      if (c < dim) {
+        const f32x4 x = Elem<WT>::load4(row, c);
+        const f32x4 dy = Elem<OT>::load4(dyrow, c);
+        const f32x4 g = gam[s * kWave + lane];
+        f32x4 xh, gg;
+        xh.x = (x.x - mu) * rs;
+        xh.y = (x.y - mu) * rs;
+        xh.z = (x.z - mu) * rs;
+        xh.w = (x.w - mu) * rs;
+        gg.x = dy.x * g.x;
+        gg.y = dy.y * g.y;
+        gg.z = dy.z * g.z;
+        gg.w = dy.w * g.w;
+        c1 = c1 + gg.x;
+        c1 = c1 + gg.y;
+        c1 = c1 + gg.z;
+        c1 = c1 + gg.w;
+        c2 = c2 + (gg.x * xh.x);
+        c2 = c2 + (gg.y * xh.y);
+        c2 = c2 + (gg.z * xh.z);
+        c2 = c2 + (gg.w * xh.w);
+        dg[s].x = dg[s].x + (dy.x * xh.x);
+        dg[s].y = dg[s].y + (dy.y * xh.y);
+        dg[s].z = dg[s].z + (dy.z * xh.z);
+        dg[s].w = dg[s].w + (dy.w * xh.w);
+        db[s].x = db[s].x + dy.x;
+        db[s].y = db[s].y + dy.y;
+        db[s].z = db[s].z + dy.z;
+        db[s].w = db[s].w + dy.w;
+      }
+    }
+    const float m1 = wave_sum(c1) / n_dim;
+    const float m2 = wave_sum(c2) / n_dim;
+    float* drow = dweight + r * dim;
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int c = s * 256 + 4 * lane;
+      if (c < dim) {
+        const f32x4 x = Elem<WT>::load4(row, c);
+        const f32x4 dy = Elem<OT>::load4(dyrow, c);
+        const f32x4 g = gam[s * kWave + lane];
+        f32x4 dx;
+        dx.x = rs * (((dy.x * g.x) - m1) - (((x.x - mu) * rs) * m2));
+        dx.y = rs * (((dy.y * g.y) - m1) - (((x.y - mu) * rs) * m2));
+        dx.z = rs * (((dy.z * g.z) - m1) - (((x.z - mu) * rs) * m2));
+        dx.w = rs * (((dy.w * g.w) - m1) - (((x.w - mu) * rs) * m2));
+        atomic_add4(drow + c, dx);
+      }
+    }
+  }
+  // combine the waves' partial sums in wave order, then write the workgroup's slot
+  for (int k = 0; k < kVecWaves; ++k) {
+    if (wave == k) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int i = s * kWave + lane;
+        if (k == 0) {
+          comb_g[i] = dg[s];
+          comb_b[i] = db[s];
+        } else {
+          comb_g[i] = comb_g[i] + dg[s];
+          comb_b[i] = comb_b[i] + db[s];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float* slot = ws + static_cast<int64_t>(blockIdx.x) * 2 * dim;
+  for (int i = threadIdx.x; i < S * kWave; i += kVecThreads) {
+    const int c = 4 * i;
+    if (c < dim) {
+      *reinterpret_cast<f32x4*>(slot + c) = comb_g[i];
+      *reinterpret_cast<f32x4*>(slot + dim + c) = comb_b[i];
+    }
+  }
+}
+
+// Element-wise backward: one wave per workgroup; the workgroup's slot in the
+// workspace accumulates its gamma and beta sums directly (only this wave touches it).
+template <typename WT, typename OT>
+__global__ void __launch_bounds__(kWave)
+bwd_elem_kernel(const WT* __restrict__ w, int64_t rows, int64_t dim, const int64_t* __restrict__ idx,
+                int64_t ntok, const float* __restrict__ gamma, const float* __restrict__ mean,
+                const float* __restrict__ rstd, const OT* __restrict__ dout,
+                float* __restrict__ dweight, float* __restrict__ ws) {
+  const int lane = threadIdx.x;
+  const float n_dim = static_cast<float>(dim);
+  float* slot_g = ws + static_cast<int64_t>(blockIdx.x) * 2 * dim;
+  float* slot_b = slot_g + dim;
+  for (int64_t c = lane; c < dim; c += kWave) {
+    slot_g[c] = 0.0f;
+    slot_b[c] = 0.0f;
+  }
+  for (int64_t t = blockIdx.x; t < ntok; t += gridDim.x) {
+    const int64_t r = idx[t];
+    if (r < 0 || r >= rows) continue;
+    const WT* row = w + r * dim;
+    const OT* dyrow = dout + t * dim;
+    const float mu = mean[t], rs = rstd[t];
+    float c1 = 0.0f, c2 = 0.0f;
+    for (int64_t c = lane; c < dim; c += kWave) {
+      const float xh = (Elem<WT>::load(row, c) - mu) * rs;
+      const float dy = Elem<OT>::load(dyrow, c);
+      const float g = dy * gamma[c];
+      c1 = c1 + g;
+      c2 = c2 + (g * xh);
+      slot_g[c] = slot_g[c] + (dy * xh);
+      slot_b[c] = slot_b[c] + dy;
+    }
+    const float m1 = wave_sum(c1) / n_dim;
+    const float m2 = wave_sum(c2) / n_dim;
+    float* drow = dweight + r * dim;
+    for (int64_t c = lane; c < dim; c += kWave) {
+      const float xh = (Elem<WT>::load(row, c) - mu) * rs;
+      const float g = Elem<OT>::load(dyrow, c) * gamma[c];
+      unsafeAtomicAdd(drow + c, rs * ((g - m1) - (xh * m2)));
+    }
+  }
+}
+
+// dgamma[c] and dbeta[c]: the slots' sums in slot order.
+__global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict__ ws,
+                                                         int64_t nslots, int64_t dim,
+                                                         float* __restrict__ dgamma,
+                                                         float* __restrict__ dbeta) {
+  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < dim;
+       c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    float a = 0.0f, b = 0.0f;
+    for (int64_t k = 0; k < nslots; ++k) {
+      a = a + ws[(2 * k) * dim + c];
+      b = b + ws[(2 * k + 1) * dim + c];
+    }
+    dgamma[c] = a;
+    dbeta[c] = b;
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_once[kMaxDevices];
+int g_cus[kMaxDevices];
+
+int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QOPT_ELAUNCH;
+  std::call_once(g_once[dev], [dev] {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+      g_cus[dev] = n;
+  });
+  if (g_cus[dev] <= 0) return QOPT_ELAUNCH;
+  *cus = g_cus[dev];
+  return QOPT_OK;
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? QOPT_OK : QOPT_ELAUNCH; }
+
+bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+size_t dtype_size(int dt) { return dt == QOPT_F32 ? 4 : 2; }
+bool dtype_ok(int dt) { return dt == QOPT_F32 || dt == QOPT_BF16; }
+
+// Slices of 256 columns for the vector kernels: the smallest of 2, 4, 8, 16 that
+// covers dim (0 if dim is too wide).
+int slices_for(int64_t dim) {
+  for (int s = 2; s <= kMaxSlices; s *= 2)
+    if (dim <= 256 * s) return s;
+  return 0;
+}
+
+template <typename K>
+int persistent_grid(K kernel, int threads, size_t lds, int64_t want, unsigned* grid) {
+  int cus = 0;
+  int rc = device_cus(&cus);
+  if (rc != QOPT_OK) return rc;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, lds) != hipSuccess ||
+      per_cu <= 0)
+    return QOPT_ELAUNCH;
+  const int64_t resident = static_cast<int64_t>(cus) * per_cu;
+  *grid = static_cast<unsigned>(want < resident ? want : resident);
+  return QOPT_OK;
+}
+
+int64_t bwd_slots(int64_t ntok, int cus) {
+  const int64_t cap = static_cast<int64_t>(cus) * kBwdSlotsPerCu;
+  return ntok < cap ? ntok : cap;
+}
+
+template <int S, typename WT, typename OT>
+int launch_fwd_vec(const void* w, int64_t rows, int64_t dim, const int64_t* idx, int64_t ntok,
+                   const float* gamma, const float* beta, float eps, void* out, float* mean,
+                   float* rstd, int32_t* bad, hipStream_t stream) {
+  auto kernel = fwd_vec_kernel<S, WT, OT>;
+  const size_t lds = 2 * S * kWave * sizeof(f32x4);
+  unsigned grid = 0;
+  int rc = persistent_grid(kernel, kVecThreads, lds, (ntok + kVecWaves - 1) / kVecWaves, &grid);
+  if (rc != QOPT_OK) return rc;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kVecThreads), lds, stream,
+                     static_cast<const WT*>(w), rows, static_cast<int32_t>(dim), idx, ntok, gamma,
+                     beta, eps, static_cast<OT*>(out), mean, rstd, bad);
+  return launch_status();
+}
+
+template <typename WT, typename OT>
+int dispatch_fwd(int S, const void* w, int64_t rows, int64_t dim, const int64_t* idx, int64_t ntok,
+                 const float* gamma, const float* beta, float eps, void* out, float* mean,
+                 float* rstd, int32_t* bad, hipStream_t stream) {
+  switch (S) {
+    case 2: return launch_fwd_vec<2, WT, OT>(w, rows, dim, idx, ntok, gamma, beta, eps, out, mean, rstd, bad, stream);
+    case 4: return launch_fwd_vec<4, WT, OT>(w, rows, dim, idx, ntok, gamma, beta, eps, out, mean, rstd, bad, stream);
+    case 8: return launch_fwd_vec<8, WT, OT>(w, rows, dim, idx, ntok, gamma, beta, eps, out, mean, rstd, bad, stream);
+    case 16: return launch_fwd_vec<16, WT, OT>(w, rows, dim, idx, ntok, gamma, beta, eps, out, mean, rstd, bad, stream);
+    default: break;
+  }
+  auto kernel = fwd_elem_kernel<WT, OT>;
+  unsigned grid = 0;
+  int rc = persistent_grid(kernel, kWave, 0, ntok, &grid);
+  if (rc != QOPT_OK) return rc;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kWave), 0, stream, static_cast<const WT*>(w), rows,
+                     dim, idx, ntok, gamma, beta, eps, static_cast<OT*>(out), mean, rstd, bad);
+  return launch_status();
+}
+
+template <int S, typename WT, typename OT>
+int launch_bwd_vec(const void* w, int64_t rows, int64_t dim, const int64_t* idx, int64_t ntok,
+                   const float* gamma, const float* mean, const float* rstd, const void* dout,
+                   float* dweight, float* ws, unsigned grid, hipStream_t stream) {
+  const size_t lds = 3 * S * kWave * sizeof(f32x4);
+  hipLaunchKernelGGL((bwd_vec_kernel<S, WT, OT>), dim3(grid), dim3(kVecThreads), lds, stream,
+                     static_cast<const WT*>(w), rows, static_cast<int32_t>(dim), idx, ntok, gamma,
+                     mean, rstd, static_cast<const OT*>(dout), dweight, ws);
+  return launch_status();
+}
+
+template <typename WT, typename OT>
+int dispatch_bwd(int S, const void* w, int64_t rows, int64_t dim, const int64_t* idx, int64_t ntok,
+                 const float* gamma, const float* mean, const float* rstd, const void* dout,
+                 float* dweight, float* ws, int cus, int64_t* nslots, hipStream_t stream) {
+  const int64_t cap = static_cast<int64_t>(cus) * kBwdSlotsPerCu;
+  if (S) {
+    const int64_t want = (ntok + kVecWaves - 1) / kVecWaves;
+    const unsigned grid = static_cast<unsigned>(want < cap ? want : cap);
+    *nslots = grid;
+    switch (S) {
+      case 2: return launch_bwd_vec<2, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, grid, stream);
+      case 4: return launch_bwd_vec<4, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, grid, stream);
+      case 8: return launch_bwd_vec<8, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, grid, stream);
+      default: return launch_bwd_vec<16, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, grid, stream);
+    }
+  }
+  const unsigned grid = static_cast<unsigned>(ntok < cap ? ntok : cap);
+  *nslots = grid;
+  hipLaunchKernelGGL((bwd_elem_kernel<WT, OT>), dim3(grid), dim3(kWave), 0, stream,
+                     static_cast<const WT*>(w), rows, dim, idx, ntok, gamma, mean, rstd,
+                     static_cast<const OT*>(dout), dweight, ws);
+  return launch_status();
+}
+
+// Vector path: width a multiple of 4 within the limit, and every row of the table
+// and of the token-major arrays aligned for 4-element accesses.
+bool vector_ok(int64_t dim, const void* w, int wdt, const void* o, int odt) {
+  return dim % 4 == 0 && slices_for(dim) != 0 && aligned(w, 4 * dtype_size(wdt)) &&
+         aligned(o, 4 * dtype_size(odt));
+}
+
+int check_common(const void* w, int wdt, int64_t rows, int64_t dim, const int64_t* idx,
+                 int64_t ntok, const float* gamma, const void* o, int odt) {
+  if (rows < 0 || dim < 0 || ntok < 0) return QOPT_EINVAL;
+  if (!dtype_ok(wdt) || !dtype_ok(odt)) return QOPT_EUNSUPPORTED;
+  if (ntok == 0) return QOPT_OK;
+  if (rows < 1 || dim < 1) return QOPT_EINVAL;
+  if (!w || !idx || !gamma || !o) return QOPT_EINVAL;
+  if (dim > (int64_t{1} << 40) / (rows > ntok ? rows : ntok)) return QOPT_EINVAL;
+  if (!aligned(w, dtype_size(wdt)) || !aligned(o, dtype_size(odt)) || !aligned(idx, 8) ||
+      !aligned(gamma, 4))
+    return QOPT_EALIGN;
+  return QOPT_OK;
+}
+
+}  // namespace
+
+extern "C" int qopt_embedding_xavier_init(void* weight_dev, int weight_dtype, int64_t rows,
+                                          int64_t dim, uint64_t seed, void* stream) {
+  if (rows < 0 || dim < 0) return QOPT_EINVAL;
+  if (!dtype_ok(weight_dtype)) return QOPT_EUNSUPPORTED;
+  if (rows == 0 || dim == 0) return QOPT_OK;
+  if (!weight_dev) return QOPT_EINVAL;
+  if (dim > (int64_t{1} << 50) / rows) return QOPT_EINVAL;
+  if (!aligned(weight_dev, dtype_size(weight_dtype))) return QOPT_EALIGN;
+  const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(dim);
+  const uint64_t nblocks = (n + 3) / 4;
+  const float a = static_cast<float>(std::sqrt(6.0 / (static_cast<double>(rows) + static_cast<double>(dim))));
+  int cus = 0;
+  int rc = device_cus(&cus);
+  if (rc != QOPT_OK) return rc;
+  const uint64_t want = (nblocks + 255) / 256;
+  const uint64_t cap = static_cast<uint64_t>(cus) * 8;
+  const unsigned grid = static_cast<unsigned>(want < cap ? want : cap);
+  const uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (weight_dtype == QOPT_F32)
+    hipLaunchKernelGGL(xavier_kernel<float>, dim3(grid), dim3(256), 0, s,
+                       static_cast<float*>(weight_dev), n, nblocks, k0, k1, a);
+  else
+    hipLaunchKernelGGL(xavier_kernel<uint16_t>, dim3(grid), dim3(256), 0, s,
+                       static_cast<uint16_t*>(weight_dev), n, nblocks, k0, k1, a);
+  return launch_status();
+}
+
+extern "C" int qopt_stable_embedding_forward(const void* weight_dev, int weight_dtype, int64_t rows,
+                                             int64_t dim, const int64_t* idx_dev, int64_t ntokens,
+                                             const float* gamma_dev, const float* beta_dev,
+                                             float eps, void* out_dev, int out_dtype,
+                                             float* mean_dev, float* rstd_dev,
+                                             int32_t* bad_count_dev, void* stream) {
+  int rc = check_common(weight_dev, weight_dtype, rows, dim, idx_dev, ntokens, gamma_dev, out_dev,
+                        out_dtype);
+  if (rc != QOPT_OK || ntokens == 0) return rc;
+  if (!beta_dev) return QOPT_EINVAL;
+  if (!std::isfinite(eps) || eps < 0.0f) return QOPT_EINVAL;
+  if ((mean_dev == nullptr) != (rstd_dev == nullptr)) return QOPT_EINVAL;
+  if (!aligned(beta_dev, 4) || !aligned(mean_dev, 4) || !aligned(rstd_dev, 4) ||
+      !aligned(bad_count_dev, 4))
+    return QOPT_EALIGN;
+  const int S = vector_ok(dim, weight_dev, weight_dtype, out_dev, out_dtype) ? slices_for(dim) : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define QOPT_FWD(WT, OT)                                                                          \
+  dispatch_fwd<WT, OT>(S, weight_dev, rows, dim, idx_dev, ntokens, gamma_dev, beta_dev, eps,      \
+                       out_dev, mean_dev, rstd_dev, bad_count_dev, s)
+  if (weight_dtype == QOPT_F32)
+    return out_dtype == QOPT_F32 ? QOPT_FWD(float, float) : QOPT_FWD(float, uint16_t);
+  return out_dtype == QOPT_F32 ? QOPT_FWD(uint16_t, float) : QOPT_FWD(uint16_t, uint16_t);
+#undef QOPT_FWD
+}
+
+extern "C" int qopt_stable_embedding_backward_workspace(int64_t ntokens, int64_t dim,
+                                                        size_t* bytes) {
+  if (!bytes || ntokens < 0 || dim < 0) return QOPT_EINVAL;
+  *bytes = 0;
+  if (ntokens == 0 || dim == 0) return QOPT_OK;
+  int cus = 0;
+  int rc = device_cus(&cus);
+  if (rc != QOPT_OK) return rc;
+  *bytes = static_cast<size_t>(bwd_slots(ntokens, cus)) * 2 * static_cast<size_t>(dim) * sizeof(float);
+  return QOPT_OK;
+}
+
+extern "C" int qopt_stable_embedding_backward(const void* weight_dev, int weight_dtype, int64_t rows,
+                                              int64_t dim, const int64_t* idx_dev, int64_t ntokens,
+                                              const float* gamma_dev, const float* mean_dev,
+                                              const float* rstd_dev, const void* dout_dev,
+                                              int dout_dtype, float* dweight_dev, float* dgamma_dev,
+                                              float* dbeta_dev, void* workspace_dev,
+                                              size_t workspace_bytes, void* stream) {
+  if (rows < 0 || dim < 0 || ntokens < 0) return QOPT_EINVAL;
+  if (!dtype_ok(weight_dtype) || !dtype_ok(dout_dtype)) return QOPT_EUNSUPPORTED;
+  if (dim == 0) return ntokens == 0 ? QOPT_OK : QOPT_EINVAL;
+  if (!dgamma_dev || !dbeta_dev) return QOPT_EINVAL;
+  if (!aligned(dgamma_dev, 4) || !aligned(dbeta_dev, 4)) return QOPT_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int cus = 0;
+  int rc = device_cus(&cus);
+  if (rc != QOPT_OK) return rc;
+  const unsigned rgrid = static_cast<unsigned>(
+      (dim + 255) / 256 < static_cast<int64_t>(cus) * 4 ? (dim + 255) / 256 : static_cast<int64_t>(cus) * 4);
+  if (ntokens == 0) {
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(rgrid), dim3(256), 0, s, nullptr, int64_t{0}, dim,
+                       dgamma_dev, dbeta_dev);
+    return launch_status();
+  }
+  rc = check_common(weight_dev, weight_dtype, rows, dim, idx_dev, ntokens, gamma_dev, dout_dev,
+                    dout_dtype);
+  if (rc != QOPT_OK) return rc;
+  if (!mean_dev || !rstd_dev || !dweight_dev || !workspace_dev) return QOPT_EINVAL;
+  if (!aligned(mean_dev, 4) || !aligned(rstd_dev, 4) || !aligned(dweight_dev, 4) ||
+      !aligned(workspace_dev, 16))
+    return QOPT_EALIGN;
+  const int64_t slots = bwd_slots(ntokens, cus);
+  if (workspace_bytes < static_cast<size_t>(slots) * 2 * static_cast<size_t>(dim) * sizeof(float))
+    return QOPT_EINVAL;
+  const bool vec = vector_ok(dim, weight_dev, weight_dtype, dout_dev, dout_dtype);
+  const int S = vec ? slices_for(dim) : 0;
+  float* ws = static_cast<float*>(workspace_dev);
+  int64_t used = 0;
+#define QOPT_BWD(WT, OT)                                                                          \
+  dispatch_bwd<WT, OT>(S, weight_dev, rows, dim, idx_dev, ntokens, gamma_dev, mean_dev, rstd_dev, \
+                       dout_dev, dweight_dev, ws, cus, &used, s)
+  if (weight_dtype == QOPT_F32)
+    rc = dout_dtype == QOPT_F32 ? QOPT_BWD(float, float) : QOPT_BWD(float, uint16_t);
+  else
+    rc = dout_dtype == QOPT_F32 ? QOPT_BWD(uint16_t, float) : QOPT_BWD(uint16_t, uint16_t);
+#undef QOPT_BWD
+  if (rc != QOPT_OK) return rc;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(rgrid), dim3(256), 0, s, ws, used, dim, dgamma_dev,
+                     dbeta_dev);
+  return launch_status();
+}

@@ -1,0 +1,313 @@
+"""GPU parity of the Stable Embedding kernels against the oracle.
+
+Initialisation is compared bit for bit.  The forward and backward passes compute in
+binary32 and are compared with the binary64 oracle within bounds derived from their
+arithmetic (see the helpers): with u = 2^-24 and k the depth of the kernels' row
+sums (per-lane sums over at most max(4 S, ceil(dim / 64)) terms, then a 6-level
+butterfly), the row mean is within (k + 1) u mean|x| of the exact one, rstd within
+(k / 2 + 7) u relative, and so on through each operation; every bound below is
+that first-order bound times 2.  Token sums (dgamma, dbeta, rows of dweight shared
+by several tokens) are bounded for any summation order by (N + 8) u times the sum
+of magnitudes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import embedding as E
+from oracle import f32_to_bf16_rne
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def q():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import block_wise_bit_adam8bit_amd as q
+    torch.cuda.set_device(0)
+    return q
+
+
+def to_dev(a, dt):
+    """float array (already representable in dt) -> device tensor of dt."""
+    if dt == "bf16":
+        return torch.from_numpy(f32_to_bf16_rne(np.asarray(a, np.float32)).view(np.int16)) \
+            .cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def depth(dim):
+    s = 2
+    while 256 * s < dim and s < 16:
+        s *= 2
+    per_lane = max(4 * s, -(-dim // 64)) if dim <= 4096 else -(-dim // 64)
+    return per_lane + 6
+
+
+def forward_tol(x, gamma, beta, eps, out_dt):
+    """Bound on |y_kernel - y_exact| per element (x: the gathered rows, binary64)."""
+    k = depth(x.shape[1])
+    y, mean, rstd, xhat = E.layer_norm_rows(x, gamma, beta, eps)
+    mabs = np.abs(x).mean(axis=1, keepdims=True)
+    tol = 2 * U * (np.abs(gamma) * ((k / 2 + 8) * np.abs(xhat) + (k + 1) * mabs * rstd[:, None])
+                   + np.abs(y) + 1e-30)
+    if out_dt == "bf16":
+        tol = tol + 2.0 ** -8 * np.abs(y) + 2.0 ** -133
+    return y, mean, rstd, tol
+
+
+def backward_ref_and_tol(x_rows, idx, rows, gamma, beta, dy, eps, base=0.0):
+    """Oracle gradients and per-element bounds for dweight (accumulated onto a table
+    holding ``base``), dgamma and dbeta."""
+    dim = x_rows.shape[1]
+    k = depth(dim)
+    _, mean, rstd, xh = E.layer_norm_rows(x_rows, gamma, beta, eps)
+    table = np.zeros((rows, dim))
+    table[idx] = x_rows
+    dw, dg, db = E.stable_embedding_backward(table, idx, gamma, beta, dy, eps)
+    g = dy * gamma
+    m2 = (g * xh).mean(axis=1, keepdims=True)
+    mabs_g = np.abs(g).mean(axis=1, keepdims=True)
+    mabs_gx = np.abs(g * xh).mean(axis=1, keepdims=True)
+    mabs_x = np.abs(x_rows).mean(axis=1, keepdims=True)
+    r = rstd[:, None]
+    dx_tol = 2 * U * (k + 16) * r * (np.abs(g) + mabs_g + np.abs(xh) * (mabs_gx + np.abs(m2))
+                                     + np.abs(m2) * mabs_x * r)
+    dx = r * (g - g.mean(axis=1, keepdims=True) - xh * m2)
+    count = np.bincount(idx, minlength=rows)[:, None]
+    dw_tol = np.zeros((rows, dim))
+    np.add.at(dw_tol, idx, dx_tol)
+    absdx = np.zeros((rows, dim))
+    np.add.at(absdx, idx, np.abs(dx))
+    dw_tol += 2 * U * count * (abs(base) + absdx)   # rounding of each accumulation
+    n = idx.size
+    dxh_tol = (k / 2 + 8) * U * np.abs(xh) + (k + 1) * U * mabs_x * r
+    dg_tol = 2 * ((np.abs(dy) * (dxh_tol + U * np.abs(xh))).sum(axis=0)
+                  + (n + 8) * U * np.abs(dy * xh).sum(axis=0))
+    db_tol = 2 * (n + 8) * U * np.abs(dy).sum(axis=0)
+    return dw, dg, db, dw_tol, dg_tol, db_tol
+
+
+def assert_within(got, want, tol, what):
+    err = np.abs(got - want)
+    bad = np.nonzero(~(err <= tol))
+    assert bad[0].size == 0, (f"{what}: {bad[0].size} elements beyond the bound, worst ratio "
+                              f"{np.max(err / np.maximum(tol, 1e-300)):.3g}")
+
+
+# ------------------------------------------------------------------ initialisation
+
+
+@pytest.mark.parametrize("rows,dim", [(1000, 96), (7, 5), (3, 1), (1, 4099)])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_xavier_init_bit_exact(q, rows, dim, dt):
+    say(f"xavier {rows}x{dim} {dt}")
+    for seed in (0, 123456789012345):
+        w = torch.empty(rows, dim, dtype=DT[dt], device="cuda")
+        q.qopt_embedding_xavier_init(w, seed)
+        want = E.xavier_uniform(rows, dim, seed)
+        if dt == "bf16":
+            got = w.view(torch.int16).cpu().numpy().view(np.uint16)
+            assert np.array_equal(got, f32_to_bf16_rne(want))
+        else:
+            assert np.array_equal(w.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------------ forward / backward
+
+
+SHAPES = [(500, 4096), (300, 2048), (200, 1000), (100, 768), (64, 96), (50, 4), (30, 5),
+          (40, 4100), (20, 6001)]
+
+
+def _inputs(rows, dim, ntok, seed):
+    rng = np.random.default_rng(seed)
+    w = rng.uniform(-0.05, 0.05, (rows, dim)).astype(np.float32)
+    w[0] += 3.0                                   # one row with a large offset
+    idx = rng.integers(0, rows, ntok).astype(np.int64)
+    idx[: min(8, ntok)] = idx[0]                  # a repeated row
+    gamma = rng.normal(1.0, 0.25, dim).astype(np.float32)
+    beta = rng.normal(0.0, 0.1, dim).astype(np.float32)
+    dy = rng.normal(0.0, 1.0, (ntok, dim)).astype(np.float32)
+    return w, idx, gamma, beta, dy
+
+
+@pytest.mark.parametrize("rows,dim", SHAPES)
+@pytest.mark.parametrize("wdt,odt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16"),
+                                     ("bf16", "f32")])
+def test_forward_and_backward(q, rows, dim, wdt, odt):
+    ntok = 300
+    say(f"stable embedding {rows}x{dim} tokens {ntok} {wdt}->{odt}")
+    w, idx, gamma, beta, dy = _inputs(rows, dim, ntok, seed=rows * 7 + dim)
+    if wdt == "bf16":
+        w = (f32_to_bf16_rne(w).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    if odt == "bf16":
+        dy = (f32_to_bf16_rne(dy).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    eps = 1e-5
+    tw, tidx = to_dev(w, wdt), torch.from_numpy(idx).cuda()
+    tg, tb = to_dev(gamma, "f32"), to_dev(beta, "f32")
+    out, mean, rstd = q.qopt_stable_embedding_forward(tw, tidx, tg, tb, eps, DT[odt])
+    x = w.astype(np.float64)[idx]
+    y, mref, rref, tol = forward_tol(x, gamma.astype(np.float64), beta.astype(np.float64), eps, odt)
+    torch.cuda.synchronize()
+    assert out.shape == (ntok, dim) and out.dtype == DT[odt]
+    assert_within(host(out), y, tol, "forward output")
+    k = depth(dim)
+    assert_within(host(mean), mref, 2 * (k + 1) * U * np.abs(x).mean(axis=1) + 1e-30, "mean")
+    assert_within(host(rstd), rref, 2 * (k / 2 + 7) * U * rref, "rstd")
+
+    tdy = to_dev(dy, odt)
+    dw0 = torch.full((rows, dim), 0.5, dtype=torch.float32, device="cuda")
+    dw, dg, db = q.qopt_stable_embedding_backward(tw, tidx, tg, mean, rstd, tdy, dweight=dw0)
+    rdw, rdg, rdb, tdw, tdg, tdb = backward_ref_and_tol(x, idx, rows, gamma.astype(np.float64),
+                                                        beta.astype(np.float64),
+                                                        dy.astype(np.float64), eps, base=0.5)
+    torch.cuda.synchronize()
+    assert dw.data_ptr() == dw0.data_ptr()
+    assert_within(host(dw) - 0.5, rdw, tdw, "dweight (accumulated onto 0.5)")
+    assert_within(host(dg), rdg, tdg, "dgamma")
+    assert_within(host(db), rdb, tdb, "dbeta")
+    # gamma and beta gradients are summed in a fixed order: a second run is identical
+    _, dg2, db2 = q.qopt_stable_embedding_backward(tw, tidx, tg, mean, rstd, tdy)
+    assert torch.equal(dg, dg2) and torch.equal(db, db2)
+
+
+def test_misaligned_views_take_the_element_path(q):
+    rows, dim, ntok = 64, 256, 100
+    w, idx, gamma, beta, dy = _inputs(rows, dim, ntok, seed=9)
+    buf = torch.zeros(rows * dim + 1, dtype=torch.float32, device="cuda")
+    tw = buf[1:].view(rows, dim)
+    tw.copy_(torch.from_numpy(w).cuda())
+    out, mean, rstd = q.qopt_stable_embedding_forward(tw, torch.from_numpy(idx).cuda(),
+                                                      to_dev(gamma, "f32"), to_dev(beta, "f32"))
+    y, _, _, tol = forward_tol(w.astype(np.float64)[idx], gamma.astype(np.float64),
+                               beta.astype(np.float64), 1e-5, "f32")
+    torch.cuda.synchronize()
+    assert_within(host(out), y, tol, "forward output (unaligned table)")
+
+
+def test_bad_indices_and_empty_batches(q):
+    rows, dim = 16, 512
+    w, _, gamma, beta, _ = _inputs(rows, dim, 4, seed=10)
+    tw, tg, tb = to_dev(w, "f32"), to_dev(gamma, "f32"), to_dev(beta, "f32")
+    idx = torch.tensor([3, -1, 16, 5, 1 << 40], dtype=torch.int64, device="cuda")
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out, mean, rstd = q.qopt_stable_embedding_forward(tw, idx, tg, tb, bad_count=bad)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 3
+    o = out.cpu().numpy()
+    assert np.isnan(o[[1, 2, 4]]).all() and np.isfinite(o[[0, 3]]).all()
+    dy = torch.ones(5, dim, device="cuda")
+    dw, dg, db = q.qopt_stable_embedding_backward(tw, idx, tg, mean, rstd, dy)
+    torch.cuda.synchronize()
+    touched = np.nonzero(np.abs(dw.cpu().numpy()).sum(axis=1))[0]
+    assert set(touched.tolist()) <= {3, 5}
+    assert np.allclose(db.cpu().numpy(), 2.0)           # only the two valid tokens
+    # no tokens: outputs empty, gamma / beta gradients zero, table gradient untouched
+    e = torch.empty(0, dtype=torch.int64, device="cuda")
+    out0, m0, r0 = q.qopt_stable_embedding_forward(tw, e, tg, tb)
+    assert out0.shape == (0, dim)
+    dw0 = torch.full((rows, dim), 2.0, device="cuda")
+    _, dg0, db0 = q.qopt_stable_embedding_backward(tw, e, tg, m0, r0,
+                                                   torch.empty(0, dim, device="cuda"), dweight=dw0)
+    torch.cuda.synchronize()
+    assert not dg0.any() and not db0.any() and bool((dw0 == 2.0).all())
+
+
+def test_module_autograd_against_oracle(q):
+    """StableEmbedding: Xavier-initialised table, LayerNorm output, gradients of all
+    three parameters through torch autograd; out-of-range ids raise."""
+    rows, dim, seed = 1000, 1024, 77
+    m = q.StableEmbedding(rows, dim, seed=seed, out_dtype=torch.bfloat16)
+    assert np.array_equal(m.weight.detach().cpu().numpy(), E.xavier_uniform(rows, dim, seed))
+    ids = workloads.zipf_token_ids(4 * 128, rows, seed=3).reshape(4, 128)
+    tids = torch.from_numpy(ids).cuda()
+    with torch.no_grad():
+        m.norm_weight.copy_(torch.linspace(0.5, 1.5, dim))
+        m.norm_bias.copy_(torch.linspace(-0.1, 0.1, dim))
+    y = m(tids)
+    assert y.shape == (4, 128, dim) and y.dtype == torch.bfloat16
+    dy = torch.randn(4, 128, dim, device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+    dy = dy.bfloat16()
+    y.backward(dy)
+    w = E.xavier_uniform(rows, dim, seed).astype(np.float64)
+    gamma = np.linspace(0.5, 1.5, dim, dtype=np.float32).astype(np.float64)
+    beta = np.linspace(-0.1, 0.1, dim, dtype=np.float32).astype(np.float64)
+    idx = ids.reshape(-1)
+    yref, _, _, tol = forward_tol(w[idx], gamma, beta, 1e-5, "bf16")
+    assert_within(host(y).reshape(-1, dim), yref, tol, "module output")
+    rdw, rdg, rdb, tdw, tdg, tdb = backward_ref_and_tol(w[idx], idx, rows, gamma, beta,
+                                                        host(dy).reshape(-1, dim), 1e-5)
+    assert_within(host(m.weight.grad), rdw, tdw, "weight grad")
+    assert_within(host(m.norm_weight.grad), rdg, tdg, "gamma grad")
+    assert_within(host(m.norm_bias.grad), rdb, tdb, "beta grad")
+    with pytest.raises(IndexError):
+        m(torch.tensor([rows], device="cuda"))
+
+
+def test_full_size_sampled(q):
+    """The Llama-7B embedding shape with 65,536 Zipf-distributed tokens, as the bench
+    runs it: sampled tokens' outputs and sampled rows' table gradients against the
+    oracle, and gamma / beta gradients over all tokens."""
+    cfg = workloads.EMBED7B
+    rows, dim, ntok = cfg["rows"], cfg["dim"], cfg["ntokens"]
+    say(f"full size {rows}x{dim}, {ntok} tokens")
+    seed = 41
+    tw = torch.empty(rows, dim, device="cuda")
+    q.qopt_embedding_xavier_init(tw, seed)
+    ids = workloads.zipf_token_ids(ntok, rows, seed=7)
+    tids = torch.from_numpy(ids).cuda()
+    tg = torch.ones(dim, device="cuda")
+    tb = torch.zeros(dim, device="cuda")
+    out, mean, rstd = q.qopt_stable_embedding_forward(tw, tids, tg, tb, 1e-5, torch.bfloat16)
+    g = torch.Generator("cuda").manual_seed(8)
+    tdy = torch.randn(ntok, dim, device="cuda", generator=g).bfloat16()
+    dw, dg, db = q.qopt_stable_embedding_backward(tw, tids, tg, mean, rstd, tdy)
+    torch.cuda.synchronize()
+    w = tw.cpu().numpy().astype(np.float64)
+    assert np.array_equal(tw.cpu().numpy(), E.xavier_uniform(rows, dim, seed))
+    gamma, beta = np.ones(dim), np.zeros(dim)
+    rng = np.random.default_rng(9)
+    toks = np.unique(np.concatenate([[0, ntok - 1], rng.choice(ntok, 512, replace=False)]))
+    y, _, _, tol = forward_tol(w[ids[toks]], gamma, beta, 1e-5, "bf16")
+    assert_within(host(out[torch.from_numpy(toks).cuda()]), y, tol, "sampled outputs")
+    dy = host(tdy)
+    # sampled rows of the table gradient: the most frequent id, a rare one, random ones
+    uniq, counts = np.unique(ids, return_counts=True)
+    pick = np.unique(np.concatenate([[uniq[np.argmax(counts)], uniq[np.argmin(counts)]],
+                                     rng.choice(uniq, 20, replace=False)]))
+    sel = np.nonzero(np.isin(ids, pick))[0]
+    rdw, _, _, tdw, _, _ = backward_ref_and_tol(w[ids[sel]], ids[sel], rows, gamma, beta,
+                                                dy[sel], 1e-5)
+    assert_within(host(dw[torch.from_numpy(pick).cuda()]), rdw[pick], tdw[pick],
+                  "sampled table-gradient rows")
+    # gamma and beta gradients over all tokens, in chunks
+    x_all = None
+    rdg = np.zeros(dim)
+    rdb = np.zeros(dim)
+    tdg = np.zeros(dim)
+    k = depth(dim)
+    for s in range(0, ntok, 8192):
+        x_all = w[ids[s:s + 8192]]
+        _, _, r, xh = E.layer_norm_rows(x_all, gamma, beta, 1e-5)
+        d = dy[s:s + 8192]
+        rdg += (d * xh).sum(axis=0)
+        rdb += d.sum(axis=0)
+        dxh = (k / 2 + 8) * U * np.abs(xh) + (k + 1) * U * np.abs(x_all).mean(axis=1,
+                                                                         keepdims=True) * r[:, None]
+        tdg += 2 * ((np.abs(d) * (dxh + U * np.abs(xh))).sum(axis=0)
+                    + (ntok + 8) * U * np.abs(d * xh).sum(axis=0))
+    assert_within(host(dg), rdg, tdg, "dgamma")
+    assert_within(host(db), rdb, 2 * (ntok + 8) * U * np.abs(dy).sum(axis=0), "dbeta")

@@ -15,19 +15,25 @@ import oracle
 qopt = pytest.importorskip("block_wise_bit_adam8bit_amd")
 from block_wise_bit_adam8bit_amd import _lib  # noqa: E402
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "qopt.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADERS = sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE) if f.endswith(".h"))
 
 
 def _declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(qopt_\w+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(qopt_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
     names = _declared_functions()
     assert {"qopt_codebook_build", "qopt_quantize_blockwise", "qopt_dequantize_blockwise",
-            "qopt_adam8bit_step", "qopt_status_string", "qopt_version"} <= set(names)
+            "qopt_adam8bit_step", "qopt_status_string", "qopt_version",
+            "qopt_embedding_xavier_init", "qopt_stable_embedding_forward",
+            "qopt_stable_embedding_backward_workspace",
+            "qopt_stable_embedding_backward"} <= set(names)
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\b[TW] (qopt_\w+)", out))
@@ -42,6 +48,7 @@ def test_header_mirror():
     assert c["QOPT_MAX_BUCKETS"] == _lib.QOPT_MAX_BUCKETS
     assert c["QOPT_THRESH_LEN"] == _lib.QOPT_THRESH_LEN
     assert c["QOPT_CODEBOOK_MAGIC"] == _lib.QOPT_CODEBOOK_MAGIC
+    assert c["QOPT_EMB_VEC_MAX_DIM"] == _lib.QOPT_EMB_VEC_MAX_DIM
     assert ctypes.sizeof(_lib.qopt_codebook) == 32 + 4 * 256 + 4 * 272 + 7168
     assert ctypes.sizeof(_lib.qopt_codebook) % 16 == 0
     assert ctypes.sizeof(_lib.qopt_tensor) == 56
@@ -203,3 +210,49 @@ def test_multi_codec_argument_checks():
         assert fn(p, nul, 1, null) == qopt.QOPT_EINVAL
         mis = (C * 1)(C(0x1002, 0x2000, 0x3000, 10))
         assert fn(p, mis, 1, null) == qopt.QOPT_EALIGN
+
+
+def test_embedding_argument_checks_before_any_device_work():
+    L = _lib.LIB
+    E = _lib
+    null = None
+    # xavier: negative sizes, unknown dtype, empty table is a no-op
+    assert L.qopt_embedding_xavier_init(null, 0, -1, 4, 0, null) == E.QOPT_EINVAL
+    assert L.qopt_embedding_xavier_init(null, 7, 4, 4, 0, null) == E.QOPT_EUNSUPPORTED
+    assert L.qopt_embedding_xavier_init(null, 0, 0, 4, 0, null) == E.QOPT_OK
+    assert L.qopt_embedding_xavier_init(null, 0, 4, 4, 0, null) == E.QOPT_EINVAL
+    assert L.qopt_embedding_xavier_init(1, 0, 4, 4, 0, null) == E.QOPT_EALIGN
+    # forward: no tokens is a no-op; bad sizes, dtypes, eps, half-given stats
+    fwd = L.qopt_stable_embedding_forward
+    assert fwd(null, 0, 10, 8, null, 0, null, null, 1e-5, null, 0, null, null, null, null) == E.QOPT_OK
+    assert fwd(null, 0, -1, 8, null, 0, null, null, 1e-5, null, 0, null, null, null, null) == E.QOPT_EINVAL
+    assert fwd(null, 3, 10, 8, null, 1, null, null, 1e-5, null, 0, null, null, null, null) == E.QOPT_EUNSUPPORTED
+    assert fwd(null, 0, 10, 8, null, 1, null, null, 1e-5, null, 0, null, null, null, null) == E.QOPT_EINVAL
+    p = 4096  # stand-in addresses: every check below fails before any dereference
+    assert fwd(p, 0, 0, 8, p, 1, p, p, 1e-5, p, 0, p, p, null, null) == E.QOPT_EINVAL
+    assert fwd(p, 0, 10, 8, p, 1, p, p, -1.0, p, 0, p, p, null, null) == E.QOPT_EINVAL
+    assert fwd(p, 0, 10, 8, p, 1, p, p, float("nan"), p, 0, p, p, null, null) == E.QOPT_EINVAL
+    assert fwd(p, 0, 10, 8, p, 1, p, p, 1e-5, p, 0, p, null, null, null) == E.QOPT_EINVAL
+    assert fwd(p + 2, 0, 10, 8, p, 1, p, p, 1e-5, p, 0, p, p, null, null) == E.QOPT_EALIGN
+    assert fwd(p, 0, 10, 8, p + 4, 1, p, p, 1e-5, p, 0, p, p, null, null) == E.QOPT_EALIGN
+    # workspace query
+    n = ctypes.c_size_t(99)
+    assert L.qopt_stable_embedding_backward_workspace(0, 8, ctypes.byref(n)) == E.QOPT_OK
+    assert n.value == 0
+    assert L.qopt_stable_embedding_backward_workspace(-1, 8, ctypes.byref(n)) == E.QOPT_EINVAL
+    assert L.qopt_stable_embedding_backward_workspace(5, 8, null) == E.QOPT_EINVAL
+    # backward: sizes, dtypes, missing gradient outputs
+    bwd = L.qopt_stable_embedding_backward
+    args = [p, 0, 10, 8, p, 1, p, p, p, p, 0, p, p, p, p, 1 << 20, null]
+    bad = list(args)
+    bad[2] = -1
+    assert bwd(*bad) == E.QOPT_EINVAL
+    bad = list(args)
+    bad[10] = 5
+    assert bwd(*bad) == E.QOPT_EUNSUPPORTED
+    bad = list(args)
+    bad[12] = null
+    assert bwd(*bad) == E.QOPT_EINVAL
+    bad = list(args)
+    bad[3] = 0
+    assert bwd(*bad) == E.QOPT_EINVAL

@@ -23,6 +23,11 @@ not throughput workloads):
                  g ~ N(0, 5e-4); the first 256,000 x 4096 elements form an embedding
                  whose gradient rows are nonzero in 2 % of the rows (5,120 rows drawn
                  per step), zero elsewhere in that region.
+* ``embed7b``    the Stable Embedding layer at the Llama-7B embedding's shape: a
+                 32,000 x 4096 table, 65,536 tokens (32 sequences of 2048) whose ids
+                 follow Zipf's law with exponent 1 over the vocabulary (ranks mapped
+                 to ids by a seeded permutation), bf16 outputs and bf16 upstream
+                 gradients ~ N(0, 1).
 """
 
 import numpy as np
@@ -168,6 +173,18 @@ def sparse_rows_mask(rows, active, seed, device):
     mask = torch.zeros(rows, dtype=torch.bool, device=device)
     mask[perm] = True
     return mask
+
+
+EMBED7B = dict(rows=32000, dim=4096, ntokens=65536)
+
+
+def zipf_token_ids(ntokens, vocab, seed, exponent=1.0):
+    """int64 token ids: rank k (1-based) has probability proportional to k^-exponent,
+    and ranks are mapped to ids by a seeded permutation of the vocabulary."""
+    rng = np.random.default_rng(seed)
+    w = 1.0 / np.arange(1, vocab + 1, dtype=np.float64) ** exponent
+    ranks = rng.choice(vocab, size=ntokens, p=w / w.sum())
+    return rng.permutation(vocab).astype(np.int64)[ranks]
 
 
 def sample_blocks(nblk, count, seed, must=()):
