@@ -270,13 +270,89 @@ def bench_convert(torch, workloads, q, args):
     print(json.dumps(out), flush=True)
 
 
+def bench_embed(torch, workloads, q, args):
+    """Stable Embedding layer at the Llama-7B embedding's shape: Xavier-initialised
+    32,000 x 4096 fp32 table, 65,536 Zipf-distributed token ids, LayerNorm forward
+    to bf16, and backward from a bf16 upstream gradient; preallocated buffers."""
+    cfg = workloads.EMBED7B
+    rows, dim, ntok = cfg["rows"], cfg["dim"], cfg["ntokens"]
+    w = torch.empty(rows, dim, dtype=torch.float32, device="cuda")
+    q.qopt_embedding_xavier_init(w, 11)
+    ids_host = workloads.zipf_token_ids(ntok, rows, seed=12)
+    ids = torch.from_numpy(ids_host).cuda()
+    gamma = torch.ones(dim, device="cuda")
+    beta = torch.zeros(dim, device="cuda")
+    out = torch.empty(ntok, dim, dtype=torch.bfloat16, device="cuda")
+    mean = torch.empty(ntok, device="cuda")
+    rstd = torch.empty(ntok, device="cuda")
+    dy = torch.empty(ntok, dim, dtype=torch.bfloat16, device="cuda")
+    workloads.fill_normal_(dy.view(-1), 1.0, 13)
+    dweight = torch.zeros(rows, dim, device="cuda")
+    dgamma = torch.empty(dim, device="cuda")
+    dbeta = torch.empty(dim, device="cuda")
+    from block_wise_bit_adam8bit_amd.embedding import backward_workspace_bytes
+    ws = torch.empty(backward_workspace_bytes(ntok, dim), dtype=torch.uint8, device="cuda")
+
+    def fwd():
+        q.qopt_stable_embedding_forward(w, ids, gamma, beta, 1e-5, torch.bfloat16,
+                                        out=out, mean=mean, rstd=rstd)
+
+    def bwd():
+        q.qopt_stable_embedding_backward(w, ids, gamma, mean, rstd, dy, dweight,
+                                         dgamma=dgamma, dbeta=dbeta, workspace=ws)
+
+    def timed(fn):
+        for _ in range(args.warmup + 1):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    tf = timed(fwd)
+    tb = timed(bwd)
+    uniq = int(len(set(ids_host.tolist())))
+    slots = ws.numel() // (2 * dim * 4)
+    # minimal HBM traffic: each distinct row once, token-major arrays once
+    fwd_bytes = uniq * dim * 4 + ntok * dim * 2 + ntok * 16 + 2 * dim * 4
+    bwd_bytes = (uniq * dim * 4 + ntok * dim * 2 + ntok * 16 + uniq * dim * 8
+                 + slots * 2 * dim * 4 * 2 + 3 * dim * 4)
+    # bytes the kernels request (every token's row read, every token's gradient row
+    # added), served partly by the caches when ids repeat
+    fwd_req = ntok * dim * (4 + 2) + ntok * 16
+    bwd_req = ntok * dim * (4 + 2 + 8) + ntok * 16
+
+    def k(ms, b, r):
+        return {"ms": round(ms, 4), "GB/s": round(b / ms / 1e6, 1),
+                "frac": round(b / ms / 1e6 / HBM_PEAK_GBS, 4),
+                "requested_GB/s": round(r / ms / 1e6, 1)}
+
+    out_line = {"metric": "stable embedding forward + backward tokens/s at 1 GPU",
+                "value": ntok / ((tf + tb) * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(tf + tb, 4),
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "f32", "data": "synthetic",
+                "config": {"workload": f"embed7b: Xavier-initialised {rows} x {dim} fp32 table, "
+                                       f"{ntok} Zipf(1) token ids ({uniq} distinct), LayerNorm "
+                                       "to bf16, bf16 upstream gradient N(0,1)",
+                           "distinct_rows": uniq, "gradient_slots": slots},
+                "kernels": {"forward": k(tf, fwd_bytes, fwd_req),
+                            "backward": k(tb, bwd_bytes, bwd_req)}}
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "gpt1p3b", "flat20b", "codec256m", "convert7b"])
+                    choices=["llama7b", "gpt1p3b", "flat20b", "codec256m", "convert7b",
+                             "embed7b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hbm-reference", action="store_true",
                     help="only time torch's copy_, fill_ and sum over 8 GiB buffers")
@@ -301,6 +377,8 @@ def main():
         return bench_codec(torch, workloads, q, args)
     if args.workload == "convert7b":
         return bench_convert(torch, workloads, q, args)
+    if args.workload == "embed7b":
+        return bench_embed(torch, workloads, q, args)
     log(f"building workload {args.workload}")
     tensors, sizes, pdt, gdt, label = make_workload(args.workload, torch, workloads)
     prepared = q.make_tensor_array(tensors)

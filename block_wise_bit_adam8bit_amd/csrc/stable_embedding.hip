@@ -22,6 +22,7 @@
 //     lane, lane + 64, ...) with the same operations.
 
 #include <hip/hip_runtime.h>
+#include <rocprim/device/device_radix_sort.hpp>
 
 #include <cmath>
 #include <cstdint>
@@ -283,120 +284,285 @@ fwd_elem_kernel(const WT* __restrict__ w, int64_t rows, int64_t dim, const int64
   }
 }
 
-__device__ __forceinline__ void atomic_add4(float* p, f32x4 v) {
-  unsafeAtomicAdd(p + 0, v.x);
-  unsafeAtomicAdd(p + 1, v.y);
-  unsafeAtomicAdd(p + 2, v.z);
-  unsafeAtomicAdd(p + 3, v.w);
+// ---- grouped backward (vector path)
+//
+// The tokens that share a row r have the same x, mean and rstd, so their summed
+// table gradient is the LayerNorm backward of S_r = sum of their upstream rows:
+//   dweight[r] += rstd * ((g - sum(g) / dim) - xhat * (sum(g * xhat) / dim)), g = S_r * gamma,
+// and dgamma = sum_r xhat_r * S_r, dbeta = sum_r S_r.  Tokens are sorted by row
+// (stable radix sort of (row, token) pairs), the sorted list is cut into chunks of
+// kSegChunk tokens, and one wave sums each chunk's runs of equal rows in registers.
+// A run that lies inside one chunk is finished by that wave; a run that crosses
+// chunk boundaries leaves per-chunk partial sums that a second kernel adds in chunk
+// order.  Every row is finished exactly once, by one wave, so dweight is updated
+// without atomics and every result is reproducible.
+
+constexpr int kSegChunk = 16;  // sorted tokens per chunk
+
+// keys[t] = idx[t] for an index in [0, rows), else rows (sorts after every valid row).
+__global__ void __launch_bounds__(256) sort_keys_kernel(const int64_t* __restrict__ idx,
+                                                        int64_t ntok, uint32_t rows,
+                                                        uint32_t* __restrict__ keys,
+                                                        int32_t* __restrict__ vals) {
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < ntok;
+       t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+    const int64_t r = idx[t];
+    keys[t] = (r >= 0 && r < static_cast<int64_t>(rows)) ? static_cast<uint32_t>(r) : rows;
+    vals[t] = static_cast<int32_t>(t);
+  }
 }
 
-template <int S, typename WT, typename OT>
-__global__ void __launch_bounds__(kVecThreads)
-bwd_vec_kernel(const WT* __restrict__ w, int64_t rows, int32_t dim, const int64_t* __restrict__ idx,
-               int64_t ntok, const float* __restrict__ gamma, const float* __restrict__ mean,
-               const float* __restrict__ rstd, const OT* __restrict__ dout,
-               float* __restrict__ dweight, float* __restrict__ ws) {
-  extern __shared__ f32x4 lds4[];
-  f32x4* gam = lds4;
-  f32x4* comb_g = lds4 + S * kWave;
-  f32x4* comb_b = lds4 + 2 * S * kWave;
-  stage4<S>(gam, gamma, dim);
-  __syncthreads();
-  const int lane = threadIdx.x % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kVecWaves;
-  const float n_dim = static_cast<float>(dim);
+// Per-wave state of the grouped kernels: gamma in LDS, the wave's dgamma / dbeta sums.
+template <int S>
+struct GroupAcc {
   f32x4 dg[S], db[S];
+};
+
+// Finish row k from its summed upstream rows acc (mean / rstd of token t, one of the
+// row's tokens): dweight row += the LayerNorm backward of acc; add its dgamma / dbeta
+// terms to the wave's sums.
+template <int S, typename WT>
+__device__ __forceinline__ void finish_row(const WT* __restrict__ w, int32_t dim, uint32_t k,
+                                           int64_t t, const f32x4 (&acc)[S], const f32x4* gam,
+                                           const float* __restrict__ mean,
+                                           const float* __restrict__ rstd,
+                                           float* __restrict__ dweight, int lane,
+                                           GroupAcc<S>& ga) {
+  const WT* row = w + static_cast<int64_t>(k) * dim;
+  const float mu = mean[t], rs = rstd[t];
+  const float n_dim = static_cast<float>(dim);
+  float c1 = 0.0f, c2 = 0.0f;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    dg[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    db[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  for (int64_t t = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave; t < ntok; t += stride) {
-    const int64_t r = idx[t];
-    if (r < 0 || r >= rows) continue;
-    const WT* row = w + r * dim;
-    const OT* dyrow = dout + t * dim;
-    const float mu = mean[t], rs = rstd[t];
-    float c1 = 0.0f, c2 = 0.0f;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int c = s * 256 + 4 * lane;
-      if (c < dim) {
-        const f32x4 x = Elem<WT>::load4(row, c);
-        const f32x4 dy = Elem<OT>::load4(dyrow, c);
-        const f32x4 g = gam[s * kWave + lane];
-        f32x4 xh, gg;
-        xh.x = (x.x - mu) * rs;
-        xh.y = (x.y - mu) * rs;
-        xh.z = (x.z - mu) * rs;
-        xh.w = (x.w - mu) * rs;
-        gg.x = dy.x * g.x;
-        gg.y = dy.y * g.y;
-        gg.z = dy.z * g.z;
-        gg.w = dy.w * g.w;
-        c1 = c1 + gg.x;
-        c1 = c1 + gg.y;
-        c1 = c1 + gg.z;
-        c1 = c1 + gg.w;
-        c2 = c2 + (gg.x * xh.x);
-        c2 = c2 + (gg.y * xh.y);
-        c2 = c2 + (gg.z * xh.z);
-        c2 = c2 + (gg.w * xh.w);
-        dg[s].x = dg[s].x + (dy.x * xh.x);
-        dg[s].y = dg[s].y + (dy.y * xh.y);
-        dg[s].z = dg[s].z + (dy.z * xh.z);
-        dg[s].w = dg[s].w + (dy.w * xh.w);
-        db[s].x = db[s].x + dy.x;
-        db[s].y = db[s].y + dy.y;
-        db[s].z = db[s].z + dy.z;
-        db[s].w = db[s].w + dy.w;
-      }
-    }
-    const float m1 = wave_sum(c1) / n_dim;
-    const float m2 = wave_sum(c2) / n_dim;
-    float* drow = dweight + r * dim;
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const int c = s * 256 + 4 * lane;
-      if (c < dim) {
-        const f32x4 x = Elem<WT>::load4(row, c);
-        const f32x4 dy = Elem<OT>::load4(dyrow, c);
-        const f32x4 g = gam[s * kWave + lane];
-        f32x4 dx;
-        dx.x = rs * (((dy.x * g.x) - m1) - (((x.x - mu) * rs) * m2));
-        dx.y = rs * (((dy.y * g.y) - m1) - (((x.y - mu) * rs) * m2));
-        dx.z = rs * (((dy.z * g.z) - m1) - (((x.z - mu) * rs) * m2));
-        dx.w = rs * (((dy.w * g.w) - m1) - (((x.w - mu) * rs) * m2));
-        atomic_add4(drow + c, dx);
-      }
+    const int c = s * 256 + 4 * lane;
+    if (c < dim) {
+      const f32x4 x = Elem<WT>::load4(row, c);
+      const f32x4 g = gam[s * kWave + lane];
+      f32x4 xh, gg;
+      xh.x = (x.x - mu) * rs;
+      xh.y = (x.y - mu) * rs;
+      xh.z = (x.z - mu) * rs;
+      xh.w = (x.w - mu) * rs;
+      gg.x = acc[s].x * g.x;
+      gg.y = acc[s].y * g.y;
+      gg.z = acc[s].z * g.z;
+      gg.w = acc[s].w * g.w;
+      c1 = c1 + gg.x;
+      c1 = c1 + gg.y;
+      c1 = c1 + gg.z;
+      c1 = c1 + gg.w;
+      c2 = c2 + (gg.x * xh.x);
+      c2 = c2 + (gg.y * xh.y);
+      c2 = c2 + (gg.z * xh.z);
+      c2 = c2 + (gg.w * xh.w);
+      ga.dg[s].x = ga.dg[s].x + (xh.x * acc[s].x);
+      ga.dg[s].y = ga.dg[s].y + (xh.y * acc[s].y);
+      ga.dg[s].z = ga.dg[s].z + (xh.z * acc[s].z);
+      ga.dg[s].w = ga.dg[s].w + (xh.w * acc[s].w);
+      ga.db[s] = ga.db[s] + acc[s];
     }
   }
-  // combine the waves' partial sums in wave order, then write the workgroup's slot
+  const float m1 = wave_sum(c1) / n_dim;
+  const float m2 = wave_sum(c2) / n_dim;
+  float* drow = dweight + static_cast<int64_t>(k) * dim;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = s * 256 + 4 * lane;
+    if (c < dim) {
+      const f32x4 x = Elem<WT>::load4(row, c);
+      const f32x4 g = gam[s * kWave + lane];
+      f32x4 d = *reinterpret_cast<const f32x4*>(drow + c);
+      d.x = d.x + (rs * (((acc[s].x * g.x) - m1) - (((x.x - mu) * rs) * m2)));
+      d.y = d.y + (rs * (((acc[s].y * g.y) - m1) - (((x.y - mu) * rs) * m2)));
+      d.z = d.z + (rs * (((acc[s].z * g.z) - m1) - (((x.z - mu) * rs) * m2)));
+      d.w = d.w + (rs * (((acc[s].w * g.w) - m1) - (((x.w - mu) * rs) * m2)));
+      *reinterpret_cast<f32x4*>(drow + c) = d;
+    }
+  }
+}
+
+// Combine the workgroup's per-wave dgamma / dbeta sums in wave order and write them
+// to workspace slot `slot` ([2][dim] floats).
+template <int S>
+__device__ __forceinline__ void write_slot(const GroupAcc<S>& ga, f32x4* comb_g, f32x4* comb_b,
+                                           float* __restrict__ slots, int64_t slot, int32_t dim,
+                                           int wave, int lane) {
   for (int k = 0; k < kVecWaves; ++k) {
     if (wave == k) {
 #pragma unroll
       for (int s = 0; s < S; ++s) {
         const int i = s * kWave + lane;
-        if (k == 0) {
-          comb_g[i] = dg[s];
-          comb_b[i] = db[s];
-        } else {
-          comb_g[i] = comb_g[i] + dg[s];
-          comb_b[i] = comb_b[i] + db[s];
-        }
+        comb_g[i] = k == 0 ? ga.dg[s] : comb_g[i] + ga.dg[s];
+        comb_b[i] = k == 0 ? ga.db[s] : comb_b[i] + ga.db[s];
       }
     }
     __syncthreads();
   }
-  float* slot = ws + static_cast<int64_t>(blockIdx.x) * 2 * dim;
+  float* out = slots + slot * 2 * dim;
   for (int i = threadIdx.x; i < S * kWave; i += kVecThreads) {
     const int c = 4 * i;
     if (c < dim) {
-      *reinterpret_cast<f32x4*>(slot + c) = comb_g[i];
-      *reinterpret_cast<f32x4*>(slot + dim + c) = comb_b[i];
+      *reinterpret_cast<f32x4*>(out + c) = comb_g[i];
+      *reinterpret_cast<f32x4*>(out + dim + c) = comb_b[i];
     }
   }
+}
+
+template <int S, typename OT>
+__device__ __forceinline__ void add_row(f32x4 (&acc)[S], const OT* __restrict__ row, int32_t dim,
+                                        int lane) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = s * 256 + 4 * lane;
+    if (c < dim) acc[s] = acc[s] + Elem<OT>::load4(row, c);
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void store_row(float* __restrict__ dst, const f32x4 (&acc)[S],
+                                          int32_t dim, int lane) {
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = s * 256 + 4 * lane;
+    if (c < dim) *reinterpret_cast<f32x4*>(dst + c) = acc[s];
+  }
+}
+
+// Chunk pass, one wave per chunk (the hardware hands workgroups to CUs as others
+// finish, which balances chunks of many short runs against chunks of one long run).
+// parts[chunk][0]: the sum over the chunk's tokens of a run that began in an earlier
+// chunk; parts[chunk][1]: of a run that begins in this chunk and goes on past it.
+template <int S, typename WT, typename OT>
+__global__ void __launch_bounds__(kVecThreads)
+group_chunk_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
+                   const uint32_t* __restrict__ keys, const int32_t* __restrict__ vals,
+                   int64_t ntok, int64_t nchunks, const float* __restrict__ gamma,
+                   const float* __restrict__ mean, const float* __restrict__ rstd,
+                   const OT* __restrict__ dout, float* __restrict__ dweight,
+                   float* __restrict__ parts, float* __restrict__ slots) {
+  extern __shared__ f32x4 lds4[];
+  f32x4* gam = lds4;
+  stage4<S>(gam, gamma, dim);
+  __syncthreads();
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  GroupAcc<S> ga;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    ga.dg[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    ga.db[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const int64_t ch = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave;
+  if (ch < nchunks) {
+    const int64_t p0 = ch * kSegChunk;
+    const int64_t p1 = p0 + kSegChunk < ntok ? p0 + kSegChunk : ntok;
+    const bool head_open = p0 > 0 && keys[p0 - 1] == keys[p0];
+    f32x4 acc[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bool first = true;
+    for (int64_t p = p0; p < p1; ++p) {
+      const uint32_t k = keys[p];
+      if (k >= rows) break;  // invalid indices sort last
+      const int64_t t = vals[p];
+      add_row<S, OT>(acc, dout + t * dim, dim, lane);
+      const bool run_ends = p + 1 == ntok || keys[p + 1] != k;
+      if (run_ends || p + 1 == p1) {
+        const bool began_here = !(first && head_open);
+        if (began_here && run_ends) {
+          finish_row<S, WT>(w, dim, k, t, acc, gam, mean, rstd, dweight, lane, ga);
+        } else {
+          store_row<S>(parts + (ch * 2 + (began_here ? 1 : 0)) * dim, acc, dim, lane);
+        }
+#pragma unroll
+        for (int s = 0; s < S; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        first = false;
+      }
+    }
+  }
+  f32x4* comb_g = lds4 + S * kWave;
+  f32x4* comb_b = lds4 + 2 * S * kWave;
+  write_slot<S>(ga, comb_g, comb_b, slots, blockIdx.x, dim, wave, lane);
+}
+
+// Is chunk ch the first chunk of a run that continues past it?  (key of that run in *k)
+__device__ __forceinline__ bool span_starts(const uint32_t* __restrict__ keys, uint32_t rows,
+                                            int64_t ntok, int64_t ch, uint32_t* k) {
+  const int64_t p0 = ch * kSegChunk;
+  const int64_t p1 = p0 + kSegChunk;
+  if (p1 >= ntok) return false;  // the last chunk has no successor
+  *k = keys[p1 - 1];
+  if (*k >= rows || keys[p1] != *k) return false;
+  return !(keys[p0] == *k && p0 > 0 && keys[p0 - 1] == *k);
+}
+
+// Runs that cross chunk boundaries, step 1: one wave per (chunk, 256-column slice)
+// adds the following chunks' head partials to the first chunk's tail partial, in
+// chunk order, and leaves the run's total in that tail slot.
+template <int S>
+__global__ void __launch_bounds__(kVecThreads)
+group_span_sum_kernel(const uint32_t* __restrict__ keys, uint32_t rows, int32_t dim,
+                      int64_t ntok, int64_t nchunks, float* __restrict__ parts) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t task = blockIdx.x * static_cast<int64_t>(kVecWaves) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int64_t ch = task / S;
+  const int s = static_cast<int>(task % S);
+  uint32_t k = 0;
+  if (ch >= nchunks || !span_starts(keys, rows, ntok, ch, &k)) return;
+  int64_t last = ch + 1;  // the run's last chunk
+  while (true) {
+    const int64_t q1 = (last + 1) * kSegChunk;
+    if (!(q1 < ntok && keys[q1 - 1] == k && keys[q1] == k)) break;
+    ++last;
+  }
+  const int c = s * 256 + 4 * lane;
+  if (c >= dim) return;
+  float* tail = parts + (ch * 2 + 1) * dim + c;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(tail);
+#pragma unroll 8
+  for (int64_t c2 = ch + 1; c2 <= last; ++c2)
+    acc = acc + *reinterpret_cast<const f32x4*>(parts + (c2 * 2) * dim + c);
+  *reinterpret_cast<f32x4*>(tail) = acc;
+}
+
+// Step 2: one wave per chunk finishes the run that starts there, from its total.
+template <int S, typename WT>
+__global__ void __launch_bounds__(kVecThreads)
+group_span_finish_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
+                         const uint32_t* __restrict__ keys, const int32_t* __restrict__ vals,
+                         int64_t ntok, int64_t nchunks, const float* __restrict__ gamma,
+                         const float* __restrict__ mean, const float* __restrict__ rstd,
+                         float* __restrict__ dweight, const float* __restrict__ parts,
+                         float* __restrict__ slots, int64_t slot0) {
+  extern __shared__ f32x4 lds4[];
+  f32x4* gam = lds4;
+  stage4<S>(gam, gamma, dim);
+  __syncthreads();
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  GroupAcc<S> ga;
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    ga.dg[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    ga.db[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  const int64_t ch = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave;
+  uint32_t k = 0;
+  if (ch < nchunks && span_starts(keys, rows, ntok, ch, &k)) {
+    const float* total = parts + (ch * 2 + 1) * dim;
+    f32x4 acc[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int c = s * 256 + 4 * lane;
+      acc[s] = c < dim ? *reinterpret_cast<const f32x4*>(total + c) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    finish_row<S, WT>(w, dim, k, vals[(ch + 1) * kSegChunk - 1], acc, gam, mean, rstd, dweight,
+                      lane, ga);
+  }
+  f32x4* comb_g = lds4 + S * kWave;
+  f32x4* comb_b = lds4 + 2 * S * kWave;
+  write_slot<S>(ga, comb_g, comb_b, slots, slot0 + blockIdx.x, dim, wave, lane);
 }
 
 // Element-wise backward: one wave per workgroup; the workgroup's slot in the
@@ -442,17 +608,50 @@ bwd_elem_kernel(const WT* __restrict__ w, int64_t rows, int64_t dim, const int64
   }
 }
 
-// dgamma[c] and dbeta[c]: the slots' sums in slot order.
-__global__ void __launch_bounds__(256) bwd_reduce_kernel(const float* __restrict__ ws,
-                                                         int64_t nslots, int64_t dim,
-                                                         float* __restrict__ dgamma,
-                                                         float* __restrict__ dbeta) {
+// dgamma[c] and dbeta[c] from the slots, in two deterministic steps.  Step 1:
+// workgroup (column block, group g) sums slots [g * per, (g + 1) * per): thread
+// (column c, subgroup j) adds the group's slots j, j + 4, ... in order, and the four
+// subgroup sums are added in subgroup order into level1[g].  Step 2 adds the groups'
+// sums in group order.
+constexpr int kReduceGroups = 64;
+
+__global__ void __launch_bounds__(256) bwd_reduce_step1_kernel(const float* __restrict__ ws,
+                                                               int64_t nslots, int64_t per,
+                                                               int64_t dim,
+                                                               float* __restrict__ level1) {
+  __shared__ float part[2][4][64];
+  const int col = threadIdx.x % 64;
+  const int sub = threadIdx.x / 64;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + col;
+  const int64_t g = blockIdx.y;
+  const int64_t k0 = g * per;
+  const int64_t k1 = k0 + per < nslots ? k0 + per : nslots;
+  float a = 0.0f, b = 0.0f;
+  if (c < dim) {
+    for (int64_t k = k0 + sub; k < k1; k += 4) {
+      a = a + ws[(2 * k) * dim + c];
+      b = b + ws[(2 * k + 1) * dim + c];
+    }
+  }
+  part[0][sub][col] = a;
+  part[1][sub][col] = b;
+  __syncthreads();
+  if (sub == 0 && c < dim) {
+    level1[(2 * g) * dim + c] = ((part[0][0][col] + part[0][1][col]) + part[0][2][col]) + part[0][3][col];
+    level1[(2 * g + 1) * dim + c] = ((part[1][0][col] + part[1][1][col]) + part[1][2][col]) + part[1][3][col];
+  }
+}
+
+__global__ void __launch_bounds__(256) bwd_reduce_step2_kernel(const float* __restrict__ level1,
+                                                               int64_t ngroups, int64_t dim,
+                                                               float* __restrict__ dgamma,
+                                                               float* __restrict__ dbeta) {
   for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < dim;
        c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     float a = 0.0f, b = 0.0f;
-    for (int64_t k = 0; k < nslots; ++k) {
-      a = a + ws[(2 * k) * dim + c];
-      b = b + ws[(2 * k + 1) * dim + c];
+    for (int64_t g = 0; g < ngroups; ++g) {
+      a = a + level1[(2 * g) * dim + c];
+      b = b + level1[(2 * g + 1) * dim + c];
     }
     dgamma[c] = a;
     dbeta[c] = b;
@@ -547,39 +746,136 @@ int dispatch_fwd(int S, const void* w, int64_t rows, int64_t dim, const int64_t*
   return launch_status();
 }
 
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Workspace of the grouped backward: sort keys and values (in and out), the radix
+// sort's own storage, the per-chunk partial sums and the dgamma / dbeta slots of the
+// two grouped kernels.
+struct GroupLayout {
+  size_t keys_in = 0, vals_in = 0, keys_out = 0, vals_out = 0, sort_tmp = 0, sort_bytes = 0;
+  size_t parts = 0, slots = 0, total = 0;
+  int64_t nchunks = 0;
+  unsigned grid = 0;
+};
+
+int group_layout(int64_t ntok, int64_t dim, GroupLayout* L) {
+  L->nchunks = (ntok + kSegChunk - 1) / kSegChunk;
+  L->grid = static_cast<unsigned>((L->nchunks + kVecWaves - 1) / kVecWaves);
+  size_t sb = 0;
+  if (rocprim::radix_sort_pairs(nullptr, sb, static_cast<const uint32_t*>(nullptr),
+                                static_cast<uint32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
+                                static_cast<int32_t*>(nullptr), static_cast<unsigned int>(ntok), 0u,
+                                32u, hipStream_t{}) != hipSuccess)
+    return QOPT_ELAUNCH;
+  const size_t n = static_cast<size_t>(ntok);
+  size_t off = 0;
+  L->keys_in = off;
+  off = align256(off + 4 * n);
+  L->vals_in = off;
+  off = align256(off + 4 * n);
+  L->keys_out = off;
+  off = align256(off + 4 * n);
+  L->vals_out = off;
+  off = align256(off + 4 * n);
+  L->sort_tmp = off;
+  L->sort_bytes = sb;
+  off = align256(off + sb);
+  L->parts = off;
+  off = align256(off + static_cast<size_t>(L->nchunks) * 2 * static_cast<size_t>(dim) * 4);
+  L->slots = off;
+  off = align256(off + 2 * static_cast<size_t>(L->grid) * 2 * static_cast<size_t>(dim) * 4);
+  L->total = off;
+  return QOPT_OK;
+}
+
+// The grouped path applies to vector-path widths, tables whose row count leaves room
+// for the invalid-index key, and token counts the radix sort takes.
+bool group_shape_ok(int64_t rows, int64_t dim, int64_t ntok) {
+  return dim % 4 == 0 && slices_for(dim) != 0 && rows < 0xFFFFFFFFll && ntok < (int64_t{1} << 31);
+}
+
 template <int S, typename WT, typename OT>
-int launch_bwd_vec(const void* w, int64_t rows, int64_t dim, const int64_t* idx, int64_t ntok,
+int launch_grouped(const void* w, int64_t rows, int64_t dim, const int64_t* idx, int64_t ntok,
                    const float* gamma, const float* mean, const float* rstd, const void* dout,
-                   float* dweight, float* ws, unsigned grid, hipStream_t stream) {
+                   float* dweight, char* ws, const GroupLayout& L, hipStream_t stream) {
+  uint32_t* keys_in = reinterpret_cast<uint32_t*>(ws + L.keys_in);
+  int32_t* vals_in = reinterpret_cast<int32_t*>(ws + L.vals_in);
+  uint32_t* keys = reinterpret_cast<uint32_t*>(ws + L.keys_out);
+  int32_t* vals = reinterpret_cast<int32_t*>(ws + L.vals_out);
+  float* parts = reinterpret_cast<float*>(ws + L.parts);
+  float* slots = reinterpret_cast<float*>(ws + L.slots);
+  const int64_t kgrid = (ntok + 255) / 256 < 4096 ? (ntok + 255) / 256 : 4096;
+  hipLaunchKernelGGL(sort_keys_kernel, dim3(static_cast<unsigned>(kgrid)), dim3(256), 0, stream,
+                     idx, ntok, static_cast<uint32_t>(rows), keys_in, vals_in);
+  int rc = launch_status();
+  if (rc != QOPT_OK) return rc;
+  size_t sb = L.sort_bytes;
+  if (rocprim::radix_sort_pairs(ws + L.sort_tmp, sb, keys_in, keys, vals_in, vals,
+                                static_cast<unsigned int>(ntok), 0u, 32u, stream) != hipSuccess)
+    return QOPT_ELAUNCH;
   const size_t lds = 3 * S * kWave * sizeof(f32x4);
-  hipLaunchKernelGGL((bwd_vec_kernel<S, WT, OT>), dim3(grid), dim3(kVecThreads), lds, stream,
-                     static_cast<const WT*>(w), rows, static_cast<int32_t>(dim), idx, ntok, gamma,
-                     mean, rstd, static_cast<const OT*>(dout), dweight, ws);
+  hipLaunchKernelGGL((group_chunk_kernel<S, WT, OT>), dim3(L.grid), dim3(kVecThreads), lds,
+                     stream, static_cast<const WT*>(w), static_cast<uint32_t>(rows),
+                     static_cast<int32_t>(dim), keys, vals, ntok, L.nchunks, gamma, mean, rstd,
+                     static_cast<const OT*>(dout), dweight, parts, slots);
+  rc = launch_status();
+  if (rc != QOPT_OK) return rc;
+  const int64_t tasks = L.nchunks * S;
+  hipLaunchKernelGGL((group_span_sum_kernel<S>), dim3(static_cast<unsigned>((tasks + kVecWaves - 1) / kVecWaves)),
+                     dim3(kVecThreads), 0, stream, keys, static_cast<uint32_t>(rows),
+                     static_cast<int32_t>(dim), ntok, L.nchunks, parts);
+  rc = launch_status();
+  if (rc != QOPT_OK) return rc;
+  hipLaunchKernelGGL((group_span_finish_kernel<S, WT>), dim3(L.grid), dim3(kVecThreads), lds,
+                     stream, static_cast<const WT*>(w), static_cast<uint32_t>(rows),
+                     static_cast<int32_t>(dim), keys, vals, ntok, L.nchunks, gamma, mean, rstd,
+                     dweight, parts, slots, static_cast<int64_t>(L.grid));
   return launch_status();
 }
 
 template <typename WT, typename OT>
 int dispatch_bwd(int S, const void* w, int64_t rows, int64_t dim, const int64_t* idx, int64_t ntok,
                  const float* gamma, const float* mean, const float* rstd, const void* dout,
-                 float* dweight, float* ws, int cus, int64_t* nslots, hipStream_t stream) {
-  const int64_t cap = static_cast<int64_t>(cus) * kBwdSlotsPerCu;
+                 float* dweight, char* ws, int cus, float** slots, int64_t* nslots,
+                 hipStream_t stream) {
   if (S) {
-    const int64_t want = (ntok + kVecWaves - 1) / kVecWaves;
-    const unsigned grid = static_cast<unsigned>(want < cap ? want : cap);
-    *nslots = grid;
+    GroupLayout L;
+    int rc = group_layout(ntok, dim, &L);
+    if (rc != QOPT_OK) return rc;
+    *slots = reinterpret_cast<float*>(ws + L.slots);
+    *nslots = 2 * static_cast<int64_t>(L.grid);
     switch (S) {
-      case 2: return launch_bwd_vec<2, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, grid, stream);
-      case 4: return launch_bwd_vec<4, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, grid, stream);
-      case 8: return launch_bwd_vec<8, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, grid, stream);
-      default: return launch_bwd_vec<16, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, grid, stream);
+      case 2: return launch_grouped<2, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, L, stream);
+      case 4: return launch_grouped<4, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, L, stream);
+      case 8: return launch_grouped<8, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, L, stream);
+      default: return launch_grouped<16, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, L, stream);
     }
   }
+  const int64_t cap = static_cast<int64_t>(cus) * kBwdSlotsPerCu;
   const unsigned grid = static_cast<unsigned>(ntok < cap ? ntok : cap);
+  *slots = reinterpret_cast<float*>(ws);
   *nslots = grid;
   hipLaunchKernelGGL((bwd_elem_kernel<WT, OT>), dim3(grid), dim3(kWave), 0, stream,
                      static_cast<const WT*>(w), rows, dim, idx, ntok, gamma, mean, rstd,
-                     static_cast<const OT*>(dout), dweight, ws);
+                     static_cast<const OT*>(dout), dweight, reinterpret_cast<float*>(ws));
   return launch_status();
+}
+
+// Workspace bytes for (ntok, dim): the larger of the grouped and element-wise needs.
+// Level-1 sums of the dgamma / dbeta reduction sit after the larger of the two paths'
+// regions; returns that offset too.
+int workspace_need(int64_t ntok, int64_t dim, int cus, size_t* bytes, size_t* level1_off = nullptr) {
+  size_t b = static_cast<size_t>(bwd_slots(ntok, cus)) * 2 * static_cast<size_t>(dim) * 4;
+  if (dim % 4 == 0 && slices_for(dim) != 0 && ntok < (int64_t{1} << 31)) {
+    GroupLayout L;
+    int rc = group_layout(ntok, dim, &L);
+    if (rc != QOPT_OK) return rc;
+    if (L.total > b) b = L.total;
+  }
+  b = align256(b);
+  if (level1_off) *level1_off = b;
+  *bytes = b + static_cast<size_t>(kReduceGroups) * 2 * static_cast<size_t>(dim) * 4;
+  return QOPT_OK;
 }
 
 // Vector path: width a multiple of 4 within the limit, and every row of the table
@@ -667,8 +963,7 @@ extern "C" int qopt_stable_embedding_backward_workspace(int64_t ntokens, int64_t
   int cus = 0;
   int rc = device_cus(&cus);
   if (rc != QOPT_OK) return rc;
-  *bytes = static_cast<size_t>(bwd_slots(ntokens, cus)) * 2 * static_cast<size_t>(dim) * sizeof(float);
-  return QOPT_OK;
+  return workspace_need(ntokens, dim, cus, bytes);
 }
 
 extern "C" int qopt_stable_embedding_backward(const void* weight_dev, int weight_dtype, int64_t rows,
@@ -690,8 +985,8 @@ extern "C" int qopt_stable_embedding_backward(const void* weight_dev, int weight
   const unsigned rgrid = static_cast<unsigned>(
       (dim + 255) / 256 < static_cast<int64_t>(cus) * 4 ? (dim + 255) / 256 : static_cast<int64_t>(cus) * 4);
   if (ntokens == 0) {
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3(rgrid), dim3(256), 0, s, nullptr, int64_t{0}, dim,
-                       dgamma_dev, dbeta_dev);
+    hipLaunchKernelGGL(bwd_reduce_step2_kernel, dim3(rgrid), dim3(256), 0, s, nullptr, int64_t{0},
+                       dim, dgamma_dev, dbeta_dev);
     return launch_status();
   }
   rc = check_common(weight_dev, weight_dtype, rows, dim, idx_dev, ntokens, gamma_dev, dout_dev,
@@ -701,23 +996,34 @@ extern "C" int qopt_stable_embedding_backward(const void* weight_dev, int weight
   if (!aligned(mean_dev, 4) || !aligned(rstd_dev, 4) || !aligned(dweight_dev, 4) ||
       !aligned(workspace_dev, 16))
     return QOPT_EALIGN;
-  const int64_t slots = bwd_slots(ntokens, cus);
-  if (workspace_bytes < static_cast<size_t>(slots) * 2 * static_cast<size_t>(dim) * sizeof(float))
-    return QOPT_EINVAL;
-  const bool vec = vector_ok(dim, weight_dev, weight_dtype, dout_dev, dout_dtype);
+  size_t need = 0, level1_off = 0;
+  rc = workspace_need(ntokens, dim, cus, &need, &level1_off);
+  if (rc != QOPT_OK) return rc;
+  if (workspace_bytes < need) return QOPT_EINVAL;
+  const bool vec = vector_ok(dim, weight_dev, weight_dtype, dout_dev, dout_dtype) &&
+                   group_shape_ok(rows, dim, ntokens) && aligned(dweight_dev, 16);
   const int S = vec ? slices_for(dim) : 0;
-  float* ws = static_cast<float*>(workspace_dev);
-  int64_t used = 0;
+  char* ws = static_cast<char*>(workspace_dev);
+  float* slots = nullptr;
+  int64_t nslots = 0;
 #define QOPT_BWD(WT, OT)                                                                          \
   dispatch_bwd<WT, OT>(S, weight_dev, rows, dim, idx_dev, ntokens, gamma_dev, mean_dev, rstd_dev, \
-                       dout_dev, dweight_dev, ws, cus, &used, s)
+                       dout_dev, dweight_dev, ws, cus, &slots, &nslots, s)
   if (weight_dtype == QOPT_F32)
     rc = dout_dtype == QOPT_F32 ? QOPT_BWD(float, float) : QOPT_BWD(float, uint16_t);
   else
     rc = dout_dtype == QOPT_F32 ? QOPT_BWD(uint16_t, float) : QOPT_BWD(uint16_t, uint16_t);
 #undef QOPT_BWD
   if (rc != QOPT_OK) return rc;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(rgrid), dim3(256), 0, s, ws, used, dim, dgamma_dev,
-                     dbeta_dev);
+  float* level1 = reinterpret_cast<float*>(ws + level1_off);
+  const int64_t per = (nslots + kReduceGroups - 1) / kReduceGroups;
+  const int64_t ngroups = (nslots + per - 1) / per;
+  hipLaunchKernelGGL(bwd_reduce_step1_kernel,
+                     dim3(static_cast<unsigned>((dim + 63) / 64), static_cast<unsigned>(ngroups)),
+                     dim3(256), 0, s, slots, nslots, per, dim, level1);
+  rc = launch_status();
+  if (rc != QOPT_OK) return rc;
+  hipLaunchKernelGGL(bwd_reduce_step2_kernel, dim3(rgrid), dim3(256), 0, s, level1, ngroups, dim,
+                     dgamma_dev, dbeta_dev);
   return launch_status();
 }

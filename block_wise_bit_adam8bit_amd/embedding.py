@@ -58,10 +58,12 @@ def qopt_embedding_xavier_init(weight, seed=0):
 
 
 def qopt_stable_embedding_forward(weight, idx, gamma, beta, eps=1e-5, out_dtype=None, *,
-                                  save_stats=True, bad_count=None):
+                                  save_stats=True, bad_count=None, out=None, mean=None,
+                                  rstd=None):
     """LayerNorm(weight[idx]): returns (out [*idx.shape, dim], mean, rstd), the last
     two [idx.numel()] float32 (None unless ``save_stats``).  ``bad_count`` (int32
-    [1] on the device) counts out-of-range indices, whose rows come out NaN."""
+    [1] on the device) counts out-of-range indices, whose rows come out NaN.  Output
+    buffers may be passed in (``out``, ``mean``, ``rstd``)."""
     out_dtype = weight.dtype if out_dtype is None else out_dtype
     _check(weight, idx, gamma, beta, bad_count)
     if weight.dim() != 2:
@@ -75,11 +77,21 @@ def qopt_stable_embedding_forward(weight, idx, gamma, beta, eps=1e-5, out_dtype=
     if bad_count is not None and (bad_count.dtype != torch.int32 or bad_count.numel() < 1):
         raise ValueError("bad_count must be an int32 device tensor")
     ntok = idx.numel()
-    out = torch.empty(*idx.shape, dim, dtype=out_dtype, device=weight.device)
-    mean = rstd = None
+    if out is None:
+        out = torch.empty(*idx.shape, dim, dtype=out_dtype, device=weight.device)
+    elif out.shape != (*idx.shape, dim) or out.dtype != out_dtype:
+        raise ValueError("out must have shape [*idx.shape, dim] and dtype out_dtype")
     if save_stats:
-        mean = torch.empty(ntok, dtype=torch.float32, device=weight.device)
-        rstd = torch.empty(ntok, dtype=torch.float32, device=weight.device)
+        if mean is None:
+            mean = torch.empty(ntok, dtype=torch.float32, device=weight.device)
+        if rstd is None:
+            rstd = torch.empty(ntok, dtype=torch.float32, device=weight.device)
+        if mean.shape != (ntok,) or rstd.shape != (ntok,) or mean.dtype != torch.float32 \
+                or rstd.dtype != torch.float32:
+            raise ValueError("mean and rstd must be float32 [ntokens]")
+    else:
+        mean = rstd = None
+    _check(out, mean, rstd)
     _lib.check("qopt_stable_embedding_forward",
                LIB.qopt_stable_embedding_forward(
                    _ptr(weight), _dtype_code(weight, "weight"), rows, dim, _ptr(idx), ntok,
@@ -96,10 +108,12 @@ def backward_workspace_bytes(ntokens, dim):
     return n.value
 
 
-def qopt_stable_embedding_backward(weight, idx, gamma, mean, rstd, dout, dweight=None):
+def qopt_stable_embedding_backward(weight, idx, gamma, mean, rstd, dout, dweight=None, *,
+                                   dgamma=None, dbeta=None, workspace=None):
     """Gradients for upstream ``dout`` [*idx.shape, dim]: returns (dweight [rows, dim]
     float32, accumulated into ``dweight`` if given, else into zeros; dgamma, dbeta
-    [dim] float32)."""
+    [dim] float32).  ``dgamma``, ``dbeta`` and a uint8 ``workspace`` of at least
+    backward_workspace_bytes(ntokens, dim) bytes may be passed in."""
     rows, dim = weight.shape
     ntok = idx.numel()
     if dweight is None:
@@ -109,10 +123,18 @@ def qopt_stable_embedding_backward(weight, idx, gamma, mean, rstd, dout, dweight
     if dout.shape != (*idx.shape, dim):
         raise ValueError("dout must have shape [*idx.shape, dim]")
     _check(weight, idx, gamma, mean, rstd, dout, dweight)
-    dgamma = torch.empty(dim, dtype=torch.float32, device=weight.device)
-    dbeta = torch.empty(dim, dtype=torch.float32, device=weight.device)
-    nbytes = backward_workspace_bytes(ntok, dim)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=weight.device)
+    if dgamma is None:
+        dgamma = torch.empty(dim, dtype=torch.float32, device=weight.device)
+    if dbeta is None:
+        dbeta = torch.empty(dim, dtype=torch.float32, device=weight.device)
+    if dgamma.shape != (dim,) or dbeta.shape != (dim,) or dgamma.dtype != torch.float32 \
+            or dbeta.dtype != torch.float32:
+        raise ValueError("dgamma and dbeta must be float32 [dim]")
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(max(backward_workspace_bytes(ntok, dim), 16), dtype=torch.uint8,
+                         device=weight.device)
+    _check(dgamma, dbeta, ws)
     _lib.check("qopt_stable_embedding_backward",
                LIB.qopt_stable_embedding_backward(
                    _ptr(weight), _dtype_code(weight, "weight"), rows, dim, _ptr(idx), ntok,

@@ -80,18 +80,24 @@ int qopt_stable_embedding_backward_workspace(int64_t ntokens, int64_t dim, size_
  * Backward of the forward above, for upstream gradient dout:
  *   xhat = (x - mean) * rstd, g = dout * gamma (x = weight[idx[t]], mean and rstd as
  *   saved by the forward), dx = rstd * ((g - sum(g) / dim) - xhat * (sum(g * xhat) / dim)),
- *   dweight[idx[t], :] += dx    (accumulated with float atomics: tokens that share a
- *                                row add up in an unspecified order),
- *   dgamma = sum over tokens of dout * xhat, dbeta = sum over tokens of dout
- *                               (written, not accumulated; summed in a fixed order,
- *                                so they are reproducible run to run).
+ *   dweight[idx[t], :] += dx, dgamma = sum over tokens of dout * xhat,
+ *   dbeta = sum over tokens of dout.
+ * Vector-path shapes (dim a multiple of 4 up to QOPT_EMB_VEC_MAX_DIM, aligned rows,
+ * dweight 16-byte aligned, rows < 2^32 - 1, ntokens < 2^31) group the tokens by row
+ * first (a stable radix sort in the workspace): the tokens of a row share x, mean and
+ * rstd, so their summed dx is the same map applied to the sum of their dout rows, and
+ * each row's gradient is formed once and added to dweight without atomics.  All
+ * three results are then reproducible run to run.  Other shapes scatter dx with
+ * float atomics (rows shared by several tokens add up in arrival order); dgamma and
+ * dbeta are still summed in a fixed order there.
  * dout_dev: [ntokens, dim] of dout_dtype.  dweight_dev: [rows, dim] float, whose
- * existing contents are added to.  dgamma_dev, dbeta_dev: [dim] float.
+ * existing contents are added to.  dgamma_dev, dbeta_dev: [dim] float (written).
  * workspace_dev: at least qopt_stable_embedding_backward_workspace(ntokens, dim)
  * bytes of device memory, 16-byte aligned; its contents are scratch.
  * Tokens whose index is outside [0, rows) contribute nothing.
  * Errors: as for the forward, plus QOPT_EINVAL for a workspace that is NULL or too
- * small.  ntokens == 0 writes zeros to dgamma and dbeta and leaves dweight as it is.
+ * small, and QOPT_ELAUNCH if the sort cannot be enqueued.  ntokens == 0 writes zeros
+ * to dgamma and dbeta and leaves dweight as it is.
  */
 int qopt_stable_embedding_backward(const void* weight_dev, int weight_dtype, int64_t rows,
                                    int64_t dim, const int64_t* idx_dev, int64_t ntokens,
