@@ -297,7 +297,8 @@ fwd_elem_kernel(const WT* __restrict__ w, int64_t rows, int64_t dim, const int64
 // order.  Every row is finished exactly once, by one wave, so dweight is updated
 // without atomics and every result is reproducible.
 
-constexpr int kSegChunk = 16;  // sorted tokens per chunk
+constexpr int kSegChunk = 16;      // sorted tokens per chunk
+constexpr int kChunkWgPerCu = 8;   // resident chunk workgroups (two waves each) per CU
 
 // keys[t] = idx[t] for an index in [0, rows), else rows (sorts after every valid row).
 __global__ void __launch_bounds__(256) sort_keys_kernel(const int64_t* __restrict__ idx,
@@ -428,61 +429,188 @@ __device__ __forceinline__ void store_row(float* __restrict__ dst, const f32x4 (
   }
 }
 
-// Chunk pass, one wave per chunk (the hardware hands workgroups to CUs as others
-// finish, which balances chunks of many short runs against chunks of one long run).
+// Raw 4-element groups of an upstream-gradient row as loaded (fp32 or packed bf16).
+template <typename OT> struct Raw4;
+template <> struct Raw4<float> {
+  typedef f32x4 type;
+  static __device__ __forceinline__ type load(const float* p, int64_t i) {
+    return *reinterpret_cast<const f32x4*>(p + i);
+  }
+  static __device__ __forceinline__ f32x4 widen(type v) { return v; }
+};
+template <> struct Raw4<uint16_t> {
+  typedef u32x2 type;
+  static __device__ __forceinline__ type load(const uint16_t* p, int64_t i) {
+    return *reinterpret_cast<const u32x2*>(p + i);
+  }
+  static __device__ __forceinline__ f32x4 widen(type w) {
+    return f32x4{bf16_bits_to_f32(w.x & 0xFFFFu), bf16_bits_to_f32(w.x >> 16),
+                 bf16_bits_to_f32(w.y & 0xFFFFu), bf16_bits_to_f32(w.y >> 16)};
+  }
+};
+
+constexpr int kPairThreads = 2 * kWave;  // chunk kernel: two waves share a chunk's columns
+
+// Chunk pass: a workgroup of two waves per chunk, walking chunks with a grid stride.
+// Wave h owns the slices h, h + 2, ... of every row (SH = S / 2 slices), so a wave
+// holds half a row of sums and can keep the next token's upstream row in flight
+// while it adds the current one.  Row-wide sums for a finished run are combined
+// across the two waves through LDS, in wave order.
 // parts[chunk][0]: the sum over the chunk's tokens of a run that began in an earlier
 // chunk; parts[chunk][1]: of a run that begins in this chunk and goes on past it.
 template <int S, typename WT, typename OT>
-__global__ void __launch_bounds__(kVecThreads)
+__global__ void __launch_bounds__(kPairThreads)
 group_chunk_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
                    const uint32_t* __restrict__ keys, const int32_t* __restrict__ vals,
                    int64_t ntok, int64_t nchunks, const float* __restrict__ gamma,
                    const float* __restrict__ mean, const float* __restrict__ rstd,
                    const OT* __restrict__ dout, float* __restrict__ dweight,
                    float* __restrict__ parts, float* __restrict__ slots) {
+  constexpr int SH = S / 2;
   extern __shared__ f32x4 lds4[];
   f32x4* gam = lds4;
+  __shared__ float red[2][2];
   stage4<S>(gam, gamma, dim);
   __syncthreads();
   const int lane = threadIdx.x % kWave;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  GroupAcc<S> ga;
+  const int h = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const float n_dim = static_cast<float>(dim);
+  f32x4 dg[SH], db[SH];
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    ga.dg[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    ga.db[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int i = 0; i < SH; ++i) {
+    dg[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    db[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  const int64_t ch = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave;
-  if (ch < nchunks) {
+  auto col = [&](int i) { return (h + 2 * i) * 256 + 4 * lane; };
+  typedef typename Raw4<OT>::type RT;
+  auto load_row = [&](RT (&dst)[SH], int64_t t) {
+    const OT* row = dout + t * dim;
+#pragma unroll
+    for (int i = 0; i < SH; ++i) {
+      if (col(i) < dim) dst[i] = Raw4<OT>::load(row, col(i));
+    }
+  };
+  for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
     const int64_t p0 = ch * kSegChunk;
     const int64_t p1 = p0 + kSegChunk < ntok ? p0 + kSegChunk : ntok;
-    const bool head_open = p0 > 0 && keys[p0 - 1] == keys[p0];
-    f32x4 acc[S];
+    // the chunk's keys (and its neighbours') and tokens, one per lane
+    const int64_t kp = p0 - 1 + lane;
+    const uint32_t key_l = (lane < kSegChunk + 2 && kp >= 0 && kp < ntok) ? keys[kp] : 0xFFFFFFFFu;
+    const int32_t val_l = (lane < kSegChunk && p0 + lane < ntok) ? vals[p0 + lane] : 0;
+    auto key_at = [&](int64_t p) {  // keys[p] for p0 - 1 <= p <= p0 + kSegChunk
+      return static_cast<uint32_t>(
+          __builtin_amdgcn_readlane(static_cast<int>(key_l), static_cast<int>(p - p0 + 1)));
+    };
+    auto tok_at = [&](int64_t p) {
+      return static_cast<int64_t>(__builtin_amdgcn_readlane(val_l, static_cast<int>(p - p0)));
+    };
+    const bool head_open = p0 > 0 && key_at(p0 - 1) == key_at(p0);
+    f32x4 acc[SH];
 #pragma unroll
-    for (int s = 0; s < S; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < SH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    RT cur[SH], nxt[SH];
+#pragma unroll
+    for (int i = 0; i < SH; ++i) {
+      cur[i] = RT{};
+      nxt[i] = RT{};
+    }
+    if (key_at(p0) < rows) load_row(cur, tok_at(p0));
     bool first = true;
     for (int64_t p = p0; p < p1; ++p) {
-      const uint32_t k = keys[p];
+      const uint32_t k = key_at(p);
       if (k >= rows) break;  // invalid indices sort last
-      const int64_t t = vals[p];
-      add_row<S, OT>(acc, dout + t * dim, dim, lane);
-      const bool run_ends = p + 1 == ntok || keys[p + 1] != k;
+      const int64_t t = tok_at(p);
+      if (p + 1 < p1 && key_at(p + 1) < rows) load_row(nxt, tok_at(p + 1));
+#pragma unroll
+      for (int i = 0; i < SH; ++i)
+        if (col(i) < dim) acc[i] = acc[i] + Raw4<OT>::widen(cur[i]);
+      const bool run_ends = p + 1 == ntok || key_at(p + 1) != k;
       if (run_ends || p + 1 == p1) {
         const bool began_here = !(first && head_open);
         if (began_here && run_ends) {
-          finish_row<S, WT>(w, dim, k, t, acc, gam, mean, rstd, dweight, lane, ga);
+          // finish row k: dweight[k] += LayerNorm backward of acc; gamma / beta terms
+          const WT* xrow = w + static_cast<int64_t>(k) * dim;
+          const float mu = mean[t], rs = rstd[t];
+          float c1 = 0.0f, c2 = 0.0f;
+#pragma unroll
+          for (int i = 0; i < SH; ++i) {
+            const int c = col(i);
+            if (c < dim) {
+              const f32x4 x = Elem<WT>::load4(xrow, c);
+              const f32x4 g = gam[(h + 2 * i) * kWave + lane];
+              f32x4 xh, gg;
+              xh.x = (x.x - mu) * rs;
+              xh.y = (x.y - mu) * rs;
+              xh.z = (x.z - mu) * rs;
+              xh.w = (x.w - mu) * rs;
+              gg.x = acc[i].x * g.x;
+              gg.y = acc[i].y * g.y;
+              gg.z = acc[i].z * g.z;
+              gg.w = acc[i].w * g.w;
+              c1 = c1 + gg.x;
+              c1 = c1 + gg.y;
+              c1 = c1 + gg.z;
+              c1 = c1 + gg.w;
+              c2 = c2 + (gg.x * xh.x);
+              c2 = c2 + (gg.y * xh.y);
+              c2 = c2 + (gg.z * xh.z);
+              c2 = c2 + (gg.w * xh.w);
+              dg[i].x = dg[i].x + (xh.x * acc[i].x);
+              dg[i].y = dg[i].y + (xh.y * acc[i].y);
+              dg[i].z = dg[i].z + (xh.z * acc[i].z);
+              dg[i].w = dg[i].w + (xh.w * acc[i].w);
+              db[i] = db[i] + acc[i];
+            }
+          }
+          c1 = wave_sum(c1);
+          c2 = wave_sum(c2);
+          if (lane == 0) {
+            red[h][0] = c1;
+            red[h][1] = c2;
+          }
+          __syncthreads();
+          const float m1 = (red[0][0] + red[1][0]) / n_dim;
+          const float m2 = (red[0][1] + red[1][1]) / n_dim;
+          __syncthreads();
+          float* drow = dweight + static_cast<int64_t>(k) * dim;
+#pragma unroll
+          for (int i = 0; i < SH; ++i) {
+            const int c = col(i);
+            if (c < dim) {
+              const f32x4 x = Elem<WT>::load4(xrow, c);
+              const f32x4 g = gam[(h + 2 * i) * kWave + lane];
+              f32x4 d = *reinterpret_cast<const f32x4*>(drow + c);
+              d.x = d.x + (rs * (((acc[i].x * g.x) - m1) - (((x.x - mu) * rs) * m2)));
+              d.y = d.y + (rs * (((acc[i].y * g.y) - m1) - (((x.y - mu) * rs) * m2)));
+              d.z = d.z + (rs * (((acc[i].z * g.z) - m1) - (((x.z - mu) * rs) * m2)));
+              d.w = d.w + (rs * (((acc[i].w * g.w) - m1) - (((x.w - mu) * rs) * m2)));
+              *reinterpret_cast<f32x4*>(drow + c) = d;
+            }
+          }
         } else {
-          store_row<S>(parts + (ch * 2 + (began_here ? 1 : 0)) * dim, acc, dim, lane);
+          float* dst = parts + (ch * 2 + (began_here ? 1 : 0)) * dim;
+#pragma unroll
+          for (int i = 0; i < SH; ++i)
+            if (col(i) < dim) *reinterpret_cast<f32x4*>(dst + col(i)) = acc[i];
         }
 #pragma unroll
-        for (int s = 0; s < S; ++s) acc[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < SH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         first = false;
       }
+#pragma unroll
+      for (int i = 0; i < SH; ++i) cur[i] = nxt[i];
     }
   }
-  f32x4* comb_g = lds4 + S * kWave;
-  f32x4* comb_b = lds4 + 2 * S * kWave;
-  write_slot<S>(ga, comb_g, comb_b, slots, blockIdx.x, dim, wave, lane);
+  // each wave writes its own columns of the workgroup's slot
+  float* out = slots + static_cast<int64_t>(blockIdx.x) * 2 * dim;
+#pragma unroll
+  for (int i = 0; i < SH; ++i) {
+    const int c = col(i);
+    if (c < dim) {
+      *reinterpret_cast<f32x4*>(out + c) = dg[i];
+      *reinterpret_cast<f32x4*>(out + dim + c) = db[i];
+    }
+  }
 }
 
 // Is chunk ch the first chunk of a run that continues past it?  (key of that run in *k)
@@ -755,12 +883,15 @@ struct GroupLayout {
   size_t keys_in = 0, vals_in = 0, keys_out = 0, vals_out = 0, sort_tmp = 0, sort_bytes = 0;
   size_t parts = 0, slots = 0, total = 0;
   int64_t nchunks = 0;
-  unsigned grid = 0;
+  unsigned grid = 0;        // chunk kernel: two-wave workgroups, persistent
+  unsigned span_grid = 0;   // span finish kernel: one wave per chunk
 };
 
-int group_layout(int64_t ntok, int64_t dim, GroupLayout* L) {
+int group_layout(int64_t ntok, int64_t dim, int cus, GroupLayout* L) {
   L->nchunks = (ntok + kSegChunk - 1) / kSegChunk;
-  L->grid = static_cast<unsigned>((L->nchunks + kVecWaves - 1) / kVecWaves);
+  const int64_t cap = static_cast<int64_t>(cus) * kChunkWgPerCu;
+  L->grid = static_cast<unsigned>(L->nchunks < cap ? L->nchunks : cap);
+  L->span_grid = static_cast<unsigned>((L->nchunks + kVecWaves - 1) / kVecWaves);
   size_t sb = 0;
   if (rocprim::radix_sort_pairs(nullptr, sb, static_cast<const uint32_t*>(nullptr),
                                 static_cast<uint32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
@@ -783,7 +914,8 @@ int group_layout(int64_t ntok, int64_t dim, GroupLayout* L) {
   L->parts = off;
   off = align256(off + static_cast<size_t>(L->nchunks) * 2 * static_cast<size_t>(dim) * 4);
   L->slots = off;
-  off = align256(off + 2 * static_cast<size_t>(L->grid) * 2 * static_cast<size_t>(dim) * 4);
+  off = align256(off + (static_cast<size_t>(L->grid) + L->span_grid) * 2 *
+                            static_cast<size_t>(dim) * 4);
   L->total = off;
   return QOPT_OK;
 }
@@ -814,8 +946,8 @@ int launch_grouped(const void* w, int64_t rows, int64_t dim, const int64_t* idx,
                                 static_cast<unsigned int>(ntok), 0u, 32u, stream) != hipSuccess)
     return QOPT_ELAUNCH;
   const size_t lds = 3 * S * kWave * sizeof(f32x4);
-  hipLaunchKernelGGL((group_chunk_kernel<S, WT, OT>), dim3(L.grid), dim3(kVecThreads), lds,
-                     stream, static_cast<const WT*>(w), static_cast<uint32_t>(rows),
+  hipLaunchKernelGGL((group_chunk_kernel<S, WT, OT>), dim3(L.grid), dim3(kPairThreads),
+                     S * kWave * sizeof(f32x4), stream, static_cast<const WT*>(w), static_cast<uint32_t>(rows),
                      static_cast<int32_t>(dim), keys, vals, ntok, L.nchunks, gamma, mean, rstd,
                      static_cast<const OT*>(dout), dweight, parts, slots);
   rc = launch_status();
@@ -826,8 +958,8 @@ int launch_grouped(const void* w, int64_t rows, int64_t dim, const int64_t* idx,
                      static_cast<int32_t>(dim), ntok, L.nchunks, parts);
   rc = launch_status();
   if (rc != QOPT_OK) return rc;
-  hipLaunchKernelGGL((group_span_finish_kernel<S, WT>), dim3(L.grid), dim3(kVecThreads), lds,
-                     stream, static_cast<const WT*>(w), static_cast<uint32_t>(rows),
+  hipLaunchKernelGGL((group_span_finish_kernel<S, WT>), dim3(L.span_grid), dim3(kVecThreads),
+                     lds, stream, static_cast<const WT*>(w), static_cast<uint32_t>(rows),
                      static_cast<int32_t>(dim), keys, vals, ntok, L.nchunks, gamma, mean, rstd,
                      dweight, parts, slots, static_cast<int64_t>(L.grid));
   return launch_status();
@@ -840,10 +972,10 @@ int dispatch_bwd(int S, const void* w, int64_t rows, int64_t dim, const int64_t*
                  hipStream_t stream) {
   if (S) {
     GroupLayout L;
-    int rc = group_layout(ntok, dim, &L);
+    int rc = group_layout(ntok, dim, cus, &L);
     if (rc != QOPT_OK) return rc;
     *slots = reinterpret_cast<float*>(ws + L.slots);
-    *nslots = 2 * static_cast<int64_t>(L.grid);
+    *nslots = static_cast<int64_t>(L.grid) + L.span_grid;
     switch (S) {
       case 2: return launch_grouped<2, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, L, stream);
       case 4: return launch_grouped<4, WT, OT>(w, rows, dim, idx, ntok, gamma, mean, rstd, dout, dweight, ws, L, stream);
@@ -868,7 +1000,7 @@ int workspace_need(int64_t ntok, int64_t dim, int cus, size_t* bytes, size_t* le
   size_t b = static_cast<size_t>(bwd_slots(ntok, cus)) * 2 * static_cast<size_t>(dim) * 4;
   if (dim % 4 == 0 && slices_for(dim) != 0 && ntok < (int64_t{1} << 31)) {
     GroupLayout L;
-    int rc = group_layout(ntok, dim, &L);
+    int rc = group_layout(ntok, dim, cus, &L);
     if (rc != QOPT_OK) return rc;
     if (L.total > b) b = L.total;
   }
