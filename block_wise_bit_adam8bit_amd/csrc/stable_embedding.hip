@@ -638,17 +638,21 @@ group_span_sum_kernel(const uint32_t* __restrict__ keys, uint32_t rows, int32_t 
   const int s = static_cast<int>(task % S);
   uint32_t k = 0;
   if (ch >= nchunks || !span_starts(keys, rows, ntok, ch, &k)) return;
-  int64_t last = ch + 1;  // the run's last chunk
-  while (true) {
-    const int64_t q1 = (last + 1) * kSegChunk;
-    if (!(q1 < ntok && keys[q1 - 1] == k && keys[q1] == k)) break;
-    ++last;
+  // the run ends at the first position past p1 whose key exceeds k (keys are sorted)
+  int64_t lo = (ch + 1) * kSegChunk, hi = ntok;
+  while (lo < hi) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (keys[mid] <= k)
+      lo = mid + 1;
+    else
+      hi = mid;
   }
+  const int64_t last = (lo - 1) / kSegChunk;  // the run's last chunk
   const int c = s * 256 + 4 * lane;
   if (c >= dim) return;
   float* tail = parts + (ch * 2 + 1) * dim + c;
   f32x4 acc = *reinterpret_cast<const f32x4*>(tail);
-#pragma unroll 8
+#pragma unroll 32
   for (int64_t c2 = ch + 1; c2 <= last; ++c2)
     acc = acc + *reinterpret_cast<const f32x4*>(parts + (c2 * 2) * dim + c);
   *reinterpret_cast<f32x4*>(tail) = acc;
