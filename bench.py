@@ -168,6 +168,46 @@ def hbm_reference(torch, reps):
     print(json.dumps({"hbm_reference": out, "buffer_bytes": 4 * n}), flush=True)
 
 
+def placements(torch, workloads, q, args):
+    """The step on several copies of the workload held at once.  Each copy is its
+    own set of allocations and so its own placement of physical memory; each copy is
+    timed in turn, twice, to separate placement from run-to-run noise."""
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    copies = []
+    for i in range(args.placements):
+        tensors, sizes, pdt, gdt, label = make_workload(args.workload, torch, workloads)
+        copies.append((tensors, q.make_tensor_array(tensors)))
+        log(f"copy {i} allocated")
+    pbytes = 4 if pdt == torch.float32 else 2
+    gbytes = 4 if gdt == torch.float32 else 2
+    step_bytes = algorithmic_bytes(sizes, pbytes, gbytes)
+    step = 0
+    for tensors, prepared in copies:
+        for _ in range(args.warmup + 1):
+            step += 1
+            q.qopt_adam8bit_step(tensors, step=step, _prepared=prepared, **hp)
+    torch.cuda.synchronize()
+    rounds = []
+    for _ in range(2):
+        row = []
+        for tensors, prepared in copies:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                step += 1
+                q.qopt_adam8bit_step(tensors, step=step, _prepared=prepared, **hp)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            row.append(round(step_bytes / ms / 1e6, 1))
+        rounds.append(row)
+    print(json.dumps({"placements": {"workload": label, "copies": args.placements,
+                                     "steps_per_timing": args.steps,
+                                     "GB/s_per_copy": rounds,
+                                     "frac_per_copy": [[round(x / HBM_PEAK_GBS, 4) for x in r]
+                                                       for r in rounds]}}), flush=True)
+
+
 def bench_codec(torch, workloads, q, args):
     """Block-wise quantize and dequantize of 2^28 values 0.01 * Student-t(3)."""
     n = 1 << 28
@@ -356,6 +396,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hbm-reference", action="store_true",
                     help="only time torch's copy_, fill_ and sum over 8 GiB buffers")
+    ap.add_argument("--placements", type=int, default=0, metavar="N",
+                    help="only time the step on N copies of the workload held at once "
+                         "(llama7b or gpt1p3b), each copy in turn")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch copies of 4 GiB (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -373,6 +416,10 @@ def main():
         return calibrate_copy(torch, args.steps)
     if args.hbm_reference:
         return hbm_reference(torch, args.steps)
+    if args.placements > 0:
+        if args.workload not in ("llama7b", "gpt1p3b"):
+            raise SystemExit("--placements takes the llama7b or gpt1p3b workload")
+        return placements(torch, workloads, q, args)
     if args.workload == "codec256m":
         return bench_codec(torch, workloads, q, args)
     if args.workload == "convert7b":
