@@ -10,8 +10,8 @@
 //     elements s*256 + 4l .. s*256 + 4l + 3 for s = 0..7, so every global access of a
 //     slice is one contiguous, fully coalesced wave-wide vector access (16 B per lane
 //     for fp32, 8 B for bf16, 4 B for codes).
-//   * A block's absmax is a max over the lane's 32 values then a butterfly across the
-//     wave: no LDS, no barrier, no other wave involved.
+//   * A block's absmax is a max over the lane's 32 values then a DPP reduction across
+//     the wave: no LDS, no barrier, no other wave involved.
 //   * Workgroups of 4 waves are persistent: each stages the codebook(s) into LDS once
 //     (the only barrier) and then walks blocks with a grid stride.
 //   * Code lookup: decode is one LDS read; encode is one LDS byte read (bucket index
@@ -36,13 +36,21 @@ constexpr int kWaves = 4;                       // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kSlices = QOPT_BLOCK / (kWave * 4);  // 8 slices of 4 elements per lane
 constexpr int kMaxTensors = 48;                 // tensors per launch (kernarg budget)
-// The step keeps a block's 32 m and v values per lane plus the prefetched inputs
-// of the next block in registers: about 240 VGPRs, so 2 waves per SIMD.  Asking
-// for 3 makes the compiler spill to scratch, which measured slower.
-#ifndef QOPT_STEP_WAVES_PER_SIMD
-#define QOPT_STEP_WAVES_PER_SIMD 2
-#endif
-constexpr int kStepWavesPerSimd = QOPT_STEP_WAVES_PER_SIMD;
+// Where the step keeps a block's second moments until the block maximum is known.
+// With fp32 parameters a lane holds its 32 m and 32 v values plus the prefetched
+// inputs of the next block in registers: about 240 VGPRs, 2 waves per SIMD.  With
+// bf16 parameters the inputs are smaller and v waits in the wave's own 8 KB of LDS
+// instead (written slice by slice after its last use in the update, read back slice
+// by slice when encoding), which brings the kernel under 168 VGPRs: 3 waves per
+// SIMD, with three 4-wave workgroups (51 KB of LDS each) per CU.
+template <typename PT> struct StepShape {
+  static constexpr bool kVInLds = false;
+  static constexpr int kWavesPerSimd = 2;
+};
+template <> struct StepShape<uint16_t> {
+  static constexpr bool kVInLds = true;
+  static constexpr int kWavesPerSimd = 3;
+};
 constexpr int kRows = static_cast<int>(sizeof(qopt_codebook) / 16);
 static_assert(kSlices * kWave * 4 == QOPT_BLOCK, "block layout");
 
@@ -105,10 +113,29 @@ __device__ __forceinline__ void stage_codebook(qopt_codebook* dst, const qopt_co
   for (int i = threadIdx.x; i < kRows; i += kThreads) d[i] = s[i];
 }
 
+// Maximum over the wave of a non-negative float (a magnitude or a second moment),
+// returned to every lane.  For non-negative binary32 values the order of the bit
+// patterns as unsigned integers is the order of the values, so the reduction runs on
+// the bits with integer max: four DPP steps inside each row of 16 lanes (swap
+// neighbours, swap pairs, mirror the half rows, mirror the rows), two row broadcasts
+// that carry the row maxima up to lane 63, then one read of lane 63 into a scalar
+// register.  No LDS traffic and no waits on it, unlike a shuffle-based butterfly.
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t u) {
+  // lanes of rows outside kRowMask read 0 (the `old` value), which leaves u unchanged
+  return umax(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+                     0, static_cast<int>(u), kCtrl, kRowMask, 0xF, false)));
+}
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
-  return x;
+  uint32_t u = __float_as_uint(x);
+  u = dpp_max<0xB1, 0xF>(u);   // quad_perm [1,0,3,2]
+  u = dpp_max<0x4E, 0xF>(u);   // quad_perm [2,3,0,1]
+  u = dpp_max<0x141, 0xF>(u);  // row_half_mirror
+  u = dpp_max<0x140, 0xF>(u);  // row_mirror
+  u = dpp_max<0x142, 0xA>(u);  // row_bcast:15 into rows 1 and 3
+  u = dpp_max<0x143, 0xC>(u);  // row_bcast:31 into rows 2 and 3
+  return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 63)));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -166,8 +193,17 @@ __device__ __forceinline__ BlockScale block_scale(float amax, uint32_t sign_mask
   return s;
 }
 
+// The sign bit is added to the bucket start before the threshold test's carry, so
+// the compare feeds one add-with-carry.  This equals (magnitude index | sign bit):
+// the magnitude index of a signed table is at most 127 and the sign mask is 0x80,
+// or the mask is 0 (an unsigned table, or a zero block).
 __device__ __forceinline__ uint32_t encode_signed(const Encoder& e, const BlockScale& s, float x) {
-  return encode_mag(e, fabsf(x) * s.r) | (x < 0.0f ? s.sign_mask : 0u);
+  const float a = fabsf(x) * s.r;
+  uint32_t i = __builtin_elementwise_sub_sat(__float_as_uint(a) >> 15, e.key0);
+  i = i < e.last_bucket ? i : e.last_bucket;
+  const uint32_t b = e.cb->bucket[i];
+  const uint32_t sign = x < 0.0f ? s.sign_mask : 0u;
+  return (b + sign) + (a >= e.cb->thresh[b + 1] ? 1u : 0u);
 }
 
 // Second moments are sums of non-negative terms, so no sign bit is ever set.
@@ -426,19 +462,15 @@ __device__ __forceinline__ void pack4(const float in[4], u32x2& v) {
   v.y = pack_bf16x2(in[2], in[3]);
 }
 
-template <typename T> __device__ __forceinline__ float load1(const void* p, int64_t i);
-template <> __device__ __forceinline__ float load1<float>(const void* p, int64_t i) {
-  return static_cast<const float*>(p)[i];
+template <typename T> __device__ __forceinline__ float load1(const T* p, int i);
+template <> __device__ __forceinline__ float load1<float>(const float* p, int i) { return p[i]; }
+template <> __device__ __forceinline__ float load1<uint16_t>(const uint16_t* p, int i) {
+  return bf16_to_f32(p[i]);
 }
-template <> __device__ __forceinline__ float load1<uint16_t>(const void* p, int64_t i) {
-  return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-}
-template <typename T> __device__ __forceinline__ void store1(void* p, int64_t i, float x);
-template <> __device__ __forceinline__ void store1<float>(void* p, int64_t i, float x) {
-  static_cast<float*>(p)[i] = x;
-}
-template <> __device__ __forceinline__ void store1<uint16_t>(void* p, int64_t i, float x) {
-  static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xFFFFu);
+template <typename T> __device__ __forceinline__ void store1(T* p, int i, float x);
+template <> __device__ __forceinline__ void store1<float>(float* p, int i, float x) { p[i] = x; }
+template <> __device__ __forceinline__ void store1<uint16_t>(uint16_t* p, int i, float x) {
+  p[i] = static_cast<uint16_t>(pack_bf16x2(x, 0.0f) & 0xFFFFu);
 }
 
 // One element of the update; returns the new parameter, leaves m and v.
@@ -535,32 +567,54 @@ struct BlockIn {
   float am, av;
 };
 
+// The lane index as a value the compiler cannot see through.  Address arithmetic
+// derived from it is then redone for each block (a few cheap ops) instead of being
+// hoisted out of the block loop, where at three waves per SIMD it would be spilled
+// to scratch and reloaded behind a wait for every outstanding load.
+__device__ __forceinline__ int opaque_lane(int lane) {
+  asm volatile("" : "+v"(lane));
+  return lane;
+}
+
 template <typename PT, typename GT>
 __device__ __forceinline__ void load_block(BlockIn<PT, GT>& in, const BlockRef& r, int lane) {
   typedef typename Vec4T<PT>::type PV;
   typedef typename Vec4T<GT>::type GV;
-  const PV* p = reinterpret_cast<const PV*>(static_cast<const PT*>(r.param) + r.base);
-  const GV* g = reinterpret_cast<const GV*>(static_cast<const GT*>(r.grad) + r.base);
-  const uint32_t* cm = reinterpret_cast<const uint32_t*>(r.cm + r.base);
-  const uint32_t* cv = reinterpret_cast<const uint32_t*>(r.cv + r.base);
+  const int l = opaque_lane(lane);
+  const PV* p = reinterpret_cast<const PV*>(static_cast<const PT*>(r.param) + r.base) + l;
+  const GV* g = reinterpret_cast<const GV*>(static_cast<const GT*>(r.grad) + r.base) + l;
+  const uint32_t* cm = reinterpret_cast<const uint32_t*>(r.cm + r.base) + l;
+  const uint32_t* cv = reinterpret_cast<const uint32_t*>(r.cv + r.base) + l;
   in.am = *r.am;
   in.av = *r.av;
 #pragma unroll
   for (int s = 0; s < kSlices; ++s) {
-    const int idx = s * kWave + lane;
-    in.p[s] = ld_wide(p + idx);
-    in.g[s] = ld_wide(g + idx);
-    in.cm[s] = ld_step_code(cm + idx);
-    in.cv[s] = ld_step_code(cv + idx);
+    in.p[s] = ld_wide(p + s * kWave);
+    in.g[s] = ld_wide(g + s * kWave);
+    in.cm[s] = ld_step_code(cm + s * kWave);
+    in.cv[s] = ld_step_code(cv + s * kWave);
   }
 }
 
-// Update of a full block from prefetched vector inputs; stores p, keeps m and v.
+// A wave's second-moment stash in LDS: slice s of lane l at 16 bytes per lane, so
+// each slice is one conflict-free 128-bit access across the wave.
+__device__ __forceinline__ void stash_v(float* vstash, int s, int lane, const float v4[4]) {
+  const f32x4 t = {v4[0], v4[1], v4[2], v4[3]};
+  reinterpret_cast<f32x4*>(vstash)[s * kWave + lane] = t;
+}
+__device__ __forceinline__ void unstash_v(const float* vstash, int s, int lane, float v4[4]) {
+  const f32x4 t = reinterpret_cast<const f32x4*>(vstash)[s * kWave + lane];
+  v4[0] = t.x; v4[1] = t.y; v4[2] = t.z; v4[3] = t.w;
+}
+
+// Update of a full block from prefetched vector inputs; stores p, keeps m and v
+// (v in the LDS stash where StepShape says so).
 template <typename PT, typename GT>
 __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_codebook& cbm,
                                            const qopt_codebook& cbv, const BlockIn<PT, GT>& in,
                                            const BlockRef& r, int lane, float m[kSlices][4],
-                                           float v[kSlices][4], float& mmax, float& vmax) {
+                                           float v[kSlices][4], float* vstash, float& mmax,
+                                           float& vmax) {
   typedef typename Vec4T<PT>::type PV;
   PV* pout = reinterpret_cast<PV*>(static_cast<PT*>(r.param) + r.base);
 #pragma unroll
@@ -627,6 +681,7 @@ __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_code
       mmax = fmaxf(mmax, fabsf(m[s][j]));
       vmax = fmaxf(vmax, v[s][j]);
     }
+    if constexpr (StepShape<PT>::kVInLds) stash_v(vstash, s, lane, v[s]);
     PV pv;
     pack4(p4, pv);
     st_wide(pout + s * kWave + lane, pv);
@@ -639,9 +694,14 @@ template <typename PT, typename GT>
 __device__ __forceinline__ void update_scalar(const AdamScalars& k, const qopt_codebook& cbm,
                                               const qopt_codebook& cbv, const BlockRef& r,
                                               int lane, float m[kSlices][4], float v[kSlices][4],
-                                              float& mmax, float& vmax) {
+                                              float* vstash, float& mmax, float& vmax) {
   const float Am = *r.am;
   const float Av = *r.av;
+  // the block's own base pointers, so that element offsets stay 32-bit
+  PT* pb = static_cast<PT*>(r.param) + r.base;
+  const GT* gb = static_cast<const GT*>(r.grad) + r.base;
+  const uint8_t* cmb = r.cm + r.base;
+  const uint8_t* cvb = r.cv + r.base;
 #pragma unroll
   for (int s = 0; s < kSlices; ++s)
 #pragma unroll
@@ -650,45 +710,53 @@ __device__ __forceinline__ void update_scalar(const AdamScalars& k, const qopt_c
       m[s][j] = 0.0f;
       v[s][j] = 0.0f;
       if (e < r.len) {
-        const int64_t i = r.base + e;
-        const float m_prev = cbm.decode[r.cm[i]] * Am;
-        const float v_prev = cbv.decode[r.cv[i]] * Av;
-        const float p = adam_element(k, load1<PT>(r.param, i), load1<GT>(r.grad, i), m_prev,
-                                     v_prev, m[s][j], v[s][j]);
-        store1<PT>(r.param, i, p);
+        const float m_prev = cbm.decode[cmb[e]] * Am;
+        const float v_prev = cbv.decode[cvb[e]] * Av;
+        const float p = adam_element(k, load1<PT>(pb, e), load1<GT>(gb, e), m_prev, v_prev,
+                                     m[s][j], v[s][j]);
+        store1<PT>(pb, e, p);
         mmax = fmaxf(mmax, fabsf(m[s][j]));
         vmax = fmaxf(vmax, v[s][j]);
       }
     }
+  if constexpr (StepShape<PT>::kVInLds) {
+#pragma unroll
+    for (int s = 0; s < kSlices; ++s) stash_v(vstash, s, lane, v[s]);
+  }
 }
 
 // Block maxima across the wave, then the codes of m and v and the new maxima.
+template <bool kVInLds>
 __device__ __forceinline__ void requantize(const Encoder& em, const Encoder& ev, uint32_t sign_m,
                                            uint32_t sign_v, const BlockRef& r, int lane,
                                            const float m[kSlices][4], const float v[kSlices][4],
-                                           float mmax, float vmax) {
+                                           const float* vstash, float mmax, float vmax) {
   const BlockScale sm = block_scale(wave_max(mmax), sign_m);
   const BlockScale sv = block_scale(wave_max(vmax), sign_v);
   uint32_t* cmo = reinterpret_cast<uint32_t*>(r.cm + r.base);
   uint32_t* cvo = reinterpret_cast<uint32_t*>(r.cv + r.base);
 #pragma unroll
   for (int s = 0; s < kSlices; ++s) {
+    float vs[4] = {v[s][0], v[s][1], v[s][2], v[s][3]};
+    if constexpr (kVInLds) unstash_v(vstash, s, lane, vs);
     uint32_t wm = 0, wv = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       wm |= encode_signed(em, sm, m[s][j]) << (8 * j);
-      wv |= encode_nonneg(ev, sv, v[s][j]) << (8 * j);
+      wv |= encode_nonneg(ev, sv, vs[j]) << (8 * j);
     }
     if (r.vec) {
       st_step_code(cmo + s * kWave + lane, wm);
       st_step_code(cvo + s * kWave + lane, wv);
-      } else {
+    } else {
+      uint8_t* cmb = r.cm + r.base;
+      uint8_t* cvb = r.cv + r.base;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = s * 256 + lane * 4 + j;
         if (e < r.len) {
-          r.cm[r.base + e] = static_cast<uint8_t>(wm >> (8 * j));
-          r.cv[r.base + e] = static_cast<uint8_t>(wv >> (8 * j));
+          cmb[e] = static_cast<uint8_t>(wm >> (8 * j));
+          cvb[e] = static_cast<uint8_t>(wv >> (8 * j));
         }
       }
     }
@@ -704,9 +772,11 @@ __device__ __forceinline__ void requantize(const Encoder& em, const Encoder& ev,
 // registers the update no longer needs), so memory stays busy through the
 // requantization phase.
 template <typename PT, typename GT>
-__global__ void __launch_bounds__(kThreads, kStepWavesPerSimd)
+__global__ void __launch_bounds__(kThreads, StepShape<PT>::kWavesPerSimd)
 adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qopt_codebook* cbv_g) {
+  constexpr bool kVInLds = StepShape<PT>::kVInLds;
   __shared__ __align__(16) qopt_codebook cb[2];
+  __shared__ __align__(16) float vstash_all[kVInLds ? kWaves * QOPT_BLOCK : 4];
   stage_codebook(&cb[0], cbm_g);
   stage_codebook(&cb[1], cbv_g);
   __syncthreads();
@@ -718,6 +788,7 @@ adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qo
   const int lane = threadIdx.x % kWave;
   const uint32_t stride = gridDim.x * kWaves;
   const uint32_t total = c.block_start[c.npieces];
+  float* vstash = kVInLds ? vstash_all + wave * QOPT_BLOCK : vstash_all;
 
   uint32_t blk = blockIdx.x * kWaves + wave;
   if (blk >= total) return;
@@ -728,9 +799,12 @@ adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qo
     float m[kSlices][4], v[kSlices][4];
     float mmax = 0.0f, vmax = 0.0f;
     if (cur.vec)
-      update_vec(k, cb[0], cb[1], in, cur, lane, m, v, mmax, vmax);
+      update_vec(k, cb[0], cb[1], in, cur, lane, m, v, vstash, mmax, vmax);
     else
-      update_scalar<PT, GT>(k, cb[0], cb[1], cur, lane, m, v, mmax, vmax);
+      update_scalar<PT, GT>(k, cb[0], cb[1], cur, lane, m, v, vstash, mmax, vmax);
+    // The stash must really go through LDS: without this the compiler may forward
+    // the stored values and keep all 32 of them live in registers.
+    if constexpr (kVInLds) asm volatile("" ::: "memory");
     const uint32_t nblk = blk + stride;
     const bool more = nblk < total;
     BlockRef nxt = cur;
@@ -738,7 +812,7 @@ adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qo
       nxt = resolve(c, nblk);
       if (nxt.vec) load_block(in, nxt, lane);
     }
-    requantize(em, ev, sign_m, sign_v, cur, lane, m, v, mmax, vmax);
+    requantize<kVInLds>(em, ev, sign_m, sign_v, cur, lane, m, v, vstash, mmax, vmax);
     if (!more) break;
     blk = nblk;
     cur = nxt;
