@@ -83,11 +83,28 @@ template <> struct Elem<uint16_t> {
   }
 };
 
-// Sum over the 64 lanes; addition is commutative, so every lane gets the same bits.
+// Sum over the 64 lanes, returned to every lane as the same bits.  Four DPP steps
+// inside each row of 16 lanes (swap neighbours, swap pairs, mirror the half rows,
+// mirror the rows) pair lanes symmetrically, so after them every lane of a row holds
+// that row's sum; two row broadcasts then add the rows up into lane 63 as
+// (r3 + r2) + (r1 + r0), and lane 63 is read into a scalar register.  Six levels of
+// additions, as in a butterfly, with no LDS traffic (a __shfl_xor butterfly compiles
+// to six dependent ds_bpermute round trips).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float x) {
+  // lanes of rows outside kRowMask read -0.0 (the `old` value), which adds nothing
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(static_cast<int>(0x80000000u),
+                                                        __float_as_int(x), kCtrl, kRowMask,
+                                                        0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) x = x + __shfl_xor(x, off, kWave);
-  return x;
+  x = dpp_add<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]
+  x = dpp_add<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]
+  x = dpp_add<0x141, 0xF>(x);  // row_half_mirror
+  x = dpp_add<0x140, 0xF>(x);  // row_mirror
+  x = dpp_add<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
 __device__ __forceinline__ float quiet_nan() { return __uint_as_float(0x7FC00000u); }

@@ -185,6 +185,26 @@ def test_misaligned_views(q):
     run_small(q, sizes, "f32", "f32", steps=3, seed=5, views=views)
 
 
+def _grads_max_at_position(n, gdt, rng):
+    """Block b's largest gradient sits at element b % 2048 of the block (signs
+    alternating), so over 2048 blocks the largest m and v of a block are held once
+    by every lane in every slice."""
+    nb = n // BLOCK
+    g = rng.normal(0, 1e-4, n).astype(np.float32)
+    b = np.arange(nb)
+    g[b * BLOCK + b % BLOCK] = np.where(b % 2 == 0, 0.1, -0.1).astype(np.float32)
+    return oracle.f32_to_bf16_rne(g) if gdt == "bf16" else g
+
+
+@pytest.mark.parametrize("pdt,gdt", [("f32", "bf16"), ("bf16", "bf16")])
+def test_block_max_at_every_position(q, pdt, gdt):
+    """The block maxima of m and v (a reduction across the wave) are exact wherever
+    in the block the maximum lies; fp32 and bf16 parameters keep v in different
+    places (registers, LDS) until the maximum is known."""
+    say(f"block max at every position {pdt}/{gdt}")
+    run_small(q, [BLOCK * BLOCK], pdt, gdt, steps=2, seed=7, grads=_grads_max_at_position)
+
+
 @pytest.mark.parametrize("hp", [dict(lr=1e-3, beta1=0.0, beta2=0.0, eps=1e-8),
                                 dict(lr=5e-2, beta1=0.5, beta2=0.75, eps=1e-6),
                                 dict(lr=1e-4, beta1=0.95, beta2=0.9999, eps=0.0)])

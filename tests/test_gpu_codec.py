@@ -55,6 +55,22 @@ def test_codec_matches_oracle(q, kind, n):
 
 
 @pytest.mark.parametrize("kind", KINDS)
+def test_block_max_at_every_position(q, kind):
+    """Block b's unique largest magnitude sits at element b of the block, so over
+    2048 blocks the maximum is held once by every lane in every slice; the block
+    maxima (a reduction across the wave) and all codes must still be exact."""
+    say(f"block max at every position, kind={kind}")
+    rng = np.random.default_rng(11)
+    x = rng.uniform(-0.5, 0.5, (workloads.BLOCK, workloads.BLOCK)).astype(np.float32)
+    b = np.arange(workloads.BLOCK)
+    x[b, b] = (np.where(b % 2 == 0, 1.0, -1.0) * (1.0 + b / 4096.0)).astype(np.float32)
+    x = x.reshape(-1)
+    if kind == oracle.UNSIGNED:
+        x = np.abs(x)
+    _check_codec(q, x, kind)
+
+
+@pytest.mark.parametrize("kind", KINDS)
 def test_codec_misaligned_views(q, kind):
     """Views at element offsets that break 16-byte (x) and 4-byte (codes) alignment
     take the element-wise path and still match."""

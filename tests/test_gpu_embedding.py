@@ -3,8 +3,8 @@
 Initialisation is compared bit for bit.  The forward and backward passes compute in
 binary32 and are compared with the binary64 oracle within bounds derived from their
 arithmetic (see the helpers): with u = 2^-24 and k the depth of the kernels' row
-sums (per-lane sums over at most max(4 S, ceil(dim / 64)) terms, then a 6-level
-butterfly), the row mean is within (k + 1) u mean|x| of the exact one, rstd within
+sums (per-lane sums over at most max(4 S, ceil(dim / 64)) terms, then 6 levels of
+additions across the wave), the row mean is within (k + 1) u mean|x| of the exact one, rstd within
 (k / 2 + 7) u relative, and so on through each operation; every bound below is
 that first-order bound times 2.  Token sums (dgamma, dbeta, rows of dweight shared
 by several tokens) are bounded for any summation order by (N + 8) u times the sum
