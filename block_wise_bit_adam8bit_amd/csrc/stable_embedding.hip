@@ -10,16 +10,18 @@
 //   - One wavefront per token row.  For rows of up to 4096 elements whose width is
 //     a multiple of 4 (the vector path), lane l holds columns s*256 + 4l .. +3 for
 //     slices s < S, in registers; row sums are a per-lane sum in slice order followed
-//     by a butterfly over the 64 lanes (every lane ends with the same bits).
+//     by a DPP reduction over the 64 lanes (every lane ends with the same bits).
 //   - Persistent workgroups walk tokens with a grid stride; gamma and beta are
 //     staged in LDS once per workgroup.
-//   - Backward: the table gradient is scattered with float atomics (rows shared by
-//     several tokens add up in arrival order); gamma and beta gradients are kept per
-//     lane in registers over a wave's tokens, combined across the workgroup's waves
-//     in wave order through LDS, written to a workspace slot per workgroup, and
-//     summed over slots in slot order by a second kernel, so they are reproducible.
+//   - Backward (vector path): tokens are sorted by table row and each row's summed
+//     upstream gradient gets one LayerNorm backward, written by one wave without
+//     atomics (see the grouped backward below); gamma and beta gradients are kept
+//     per lane in registers over a wave's rows, written to a workspace slot per
+//     workgroup and summed over slots in slot order, so all three gradients are
+//     reproducible bit for bit.
 //   - Every other shape runs element-wise kernels (one wave per workgroup, columns
-//     lane, lane + 64, ...) with the same operations.
+//     lane, lane + 64, ...) with the same operations; their table gradient is
+//     scattered with float atomics.
 
 #include <hip/hip_runtime.h>
 #include <rocprim/device/device_radix_sort.hpp>
@@ -468,15 +470,31 @@ template <> struct Raw4<uint16_t> {
 
 constexpr int kPairThreads = 2 * kWave;  // chunk kernel: two waves share a chunk's columns
 
+// An int the compiler cannot see through.  Addresses derived from it inside a loop
+// are redone per iteration (a few cheap ops) instead of being hoisted out of the
+// loop as 64-bit offsets per slice, which would pin dozens of registers.
+__device__ __forceinline__ int opaque_int(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Chunk pass: a workgroup of two waves per chunk, walking chunks with a grid stride.
 // Wave h owns the slices h, h + 2, ... of every row (SH = S / 2 slices), so a wave
-// holds half a row of sums and can keep the next token's upstream row in flight
-// while it adds the current one.  Row-wide sums for a finished run are combined
-// across the two waves through LDS, in wave order.
+// holds half a row of sums and keeps the next token's upstream row in flight while
+// it adds the current one.  The loads and adds of the token loop have no branches
+// (a slice past the row's end reads the row's first columns and adds zero) and the
+// loads are unconditional, so the compiler waits for exactly the row it adds; with
+// a branch per slice it waits for every outstanding load, the prefetched row
+// included.  Row-wide sums for a finished run are combined across the two waves
+// through LDS, in wave order.
 // parts[chunk][0]: the sum over the chunk's tokens of a run that began in an earlier
 // chunk; parts[chunk][1]: of a run that begins in this chunk and goes on past it.
+// bf16 upstream rows leave room for 3 waves per SIMD (under 168 VGPRs with no
+// scratch); fp32 ones hold twice the registers per row in flight and keep 2.
+template <typename OT> constexpr int chunk_waves_per_simd() { return sizeof(OT) == 2 ? 3 : 2; }
+
 template <int S, typename WT, typename OT>
-__global__ void __launch_bounds__(kPairThreads)
+__global__ void __launch_bounds__(kPairThreads, chunk_waves_per_simd<OT>())
 group_chunk_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
                    const uint32_t* __restrict__ keys, const int32_t* __restrict__ vals,
                    int64_t ntok, int64_t nchunks, const float* __restrict__ gamma,
@@ -498,14 +516,16 @@ group_chunk_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
     dg[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     db[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  auto col = [&](int i) { return (h + 2 * i) * 256 + 4 * lane; };
+  // this lane's first column; slice i of the wave starts 512 columns further on
+  const int col0 = h * 256 + 4 * lane;
+  auto col = [&](int i) { return col0 + 512 * i; };
   typedef typename Raw4<OT>::type RT;
   auto load_row = [&](RT (&dst)[SH], int64_t t) {
+    const int c0 = opaque_int(col0);
     const OT* row = dout + t * dim;
 #pragma unroll
-    for (int i = 0; i < SH; ++i) {
-      if (col(i) < dim) dst[i] = Raw4<OT>::load(row, col(i));
-    }
+    for (int i = 0; i < SH; ++i)
+      dst[i] = Raw4<OT>::load(row, c0 + 512 * i < dim ? c0 + 512 * i : 0);
   };
   for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
     const int64_t p0 = ch * kSegChunk;
@@ -525,35 +545,48 @@ group_chunk_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
     f32x4 acc[SH];
 #pragma unroll
     for (int i = 0; i < SH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    RT cur[SH], nxt[SH];
+    // two row buffers: token p's row is added from one while token p + 1's is in
+    // flight in the other; the loop is unrolled by two so that the buffers swap
+    // roles without copies (copying a register whose load is still pending would
+    // wait for it)
+    RT b0[SH], b1[SH];
 #pragma unroll
     for (int i = 0; i < SH; ++i) {
-      cur[i] = RT{};
-      nxt[i] = RT{};
+      b0[i] = RT{};
+      b1[i] = RT{};
     }
-    if (key_at(p0) < rows) load_row(cur, tok_at(p0));
+    // The loads are unconditional, so that the compiler can count them and wait for
+    // exactly the row it adds: past the chunk's end a step reloads the row it has
+    // just used (a cache hit).  Every token position is a valid upstream row.
+    load_row(b0, tok_at(p0));
     bool first = true;
-    for (int64_t p = p0; p < p1; ++p) {
+    // token p: start loading token p + 1's row into `fill`, add token p's row (in
+    // `use`), finish or hand on the run if it ends here; false at the first invalid
+    // index (they sort last)
+    auto step = [&](int64_t p, const RT (&use)[SH], RT (&fill)[SH]) -> bool {
       const uint32_t k = key_at(p);
-      if (k >= rows) break;  // invalid indices sort last
+      if (k >= rows) return false;
       const int64_t t = tok_at(p);
-      if (p + 1 < p1 && key_at(p + 1) < rows) load_row(nxt, tok_at(p + 1));
+      load_row(fill, p + 1 < p1 ? tok_at(p + 1) : t);
 #pragma unroll
-      for (int i = 0; i < SH; ++i)
-        if (col(i) < dim) acc[i] = acc[i] + Raw4<OT>::widen(cur[i]);
+      for (int i = 0; i < SH; ++i) {
+        const f32x4 r = Raw4<OT>::widen(use[i]);
+        const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+        acc[i] = acc[i] + (col(i) < dim ? r : zero);
+      }
       const bool run_ends = p + 1 == ntok || key_at(p + 1) != k;
       if (run_ends || p + 1 == p1) {
         const bool began_here = !(first && head_open);
         if (began_here && run_ends) {
           // finish row k: dweight[k] += LayerNorm backward of acc; gamma / beta terms
-          const WT* xrow = w + static_cast<int64_t>(k) * dim;
+          const int c0 = opaque_int(col0);
+          const WT* xrow = w + static_cast<int64_t>(k) * dim + c0;
           const float mu = mean[t], rs = rstd[t];
           float c1 = 0.0f, c2 = 0.0f;
 #pragma unroll
           for (int i = 0; i < SH; ++i) {
-            const int c = col(i);
-            if (c < dim) {
-              const f32x4 x = Elem<WT>::load4(xrow, c);
+            if (c0 + 512 * i < dim) {
+              const f32x4 x = Elem<WT>::load4(xrow, 512 * i);
               const f32x4 g = gam[(h + 2 * i) * kWave + lane];
               f32x4 xh, gg;
               xh.x = (x.x - mu) * rs;
@@ -589,33 +622,36 @@ group_chunk_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
           const float m1 = (red[0][0] + red[1][0]) / n_dim;
           const float m2 = (red[0][1] + red[1][1]) / n_dim;
           __syncthreads();
-          float* drow = dweight + static_cast<int64_t>(k) * dim;
+          float* drow = dweight + static_cast<int64_t>(k) * dim + c0;
 #pragma unroll
           for (int i = 0; i < SH; ++i) {
-            const int c = col(i);
-            if (c < dim) {
-              const f32x4 x = Elem<WT>::load4(xrow, c);
+            if (c0 + 512 * i < dim) {
+              const f32x4 x = Elem<WT>::load4(xrow, 512 * i);
               const f32x4 g = gam[(h + 2 * i) * kWave + lane];
-              f32x4 d = *reinterpret_cast<const f32x4*>(drow + c);
+              f32x4 d = *reinterpret_cast<const f32x4*>(drow + 512 * i);
               d.x = d.x + (rs * (((acc[i].x * g.x) - m1) - (((x.x - mu) * rs) * m2)));
               d.y = d.y + (rs * (((acc[i].y * g.y) - m1) - (((x.y - mu) * rs) * m2)));
               d.z = d.z + (rs * (((acc[i].z * g.z) - m1) - (((x.z - mu) * rs) * m2)));
               d.w = d.w + (rs * (((acc[i].w * g.w) - m1) - (((x.w - mu) * rs) * m2)));
-              *reinterpret_cast<f32x4*>(drow + c) = d;
+              *reinterpret_cast<f32x4*>(drow + 512 * i) = d;
             }
           }
         } else {
-          float* dst = parts + (ch * 2 + (began_here ? 1 : 0)) * dim;
+          const int c0 = opaque_int(col0);
+          float* dst = parts + (ch * 2 + (began_here ? 1 : 0)) * dim + c0;
 #pragma unroll
           for (int i = 0; i < SH; ++i)
-            if (col(i) < dim) *reinterpret_cast<f32x4*>(dst + col(i)) = acc[i];
+            if (c0 + 512 * i < dim) *reinterpret_cast<f32x4*>(dst + 512 * i) = acc[i];
         }
 #pragma unroll
         for (int i = 0; i < SH; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         first = false;
       }
-#pragma unroll
-      for (int i = 0; i < SH; ++i) cur[i] = nxt[i];
+      return true;
+    };
+    for (int64_t p = p0; p < p1; p += 2) {
+      if (!step(p, b0, b1)) break;
+      if (p + 1 >= p1 || !step(p + 1, b1, b0)) break;
     }
   }
   // each wave writes its own columns of the workgroup's slot
