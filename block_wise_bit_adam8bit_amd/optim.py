@@ -64,12 +64,15 @@ class Adam8bit(torch.optim.Optimizer):
                      st["v_absmax"]))
             b1, b2 = group["betas"]
             for key, items in batches.items():
-                sig = (gi, key[:3], tuple(t[0].data_ptr() for t in items),
-                       tuple(t[1].data_ptr() for t in items))
+                # launch descriptors are cached per batch (group, device, dtypes and
+                # parameters) and rebuilt when its gradients move
+                ident = (gi, key[:3], tuple(t[0].data_ptr() for t in items))
+                sig = ident + (tuple(t[1].data_ptr() for t in items),)
                 prepared = self._prepared.get(sig)
                 if prepared is None:
                     prepared = make_tensor_array(items)
-                    self._prepared = {k: v for k, v in self._prepared.items() if k[0] != gi}
+                    self._prepared = {k: v for k, v in self._prepared.items()
+                                      if k[:3] != ident}
                     self._prepared[sig] = prepared
                 qopt_adam8bit_step(items, lr=group["lr"], beta1=b1, beta2=b2, eps=group["eps"],
                                    step=key[3], _prepared=prepared)

@@ -308,6 +308,59 @@ def test_optimizer_class_and_resume(q):
     assert torch.equal(w.detach(), final_w) and torch.equal(b.detach(), final_b)
 
 
+def test_optimizer_per_parameter_steps(q):
+    """A parameter without a gradient skips the step and keeps its own step count
+    (as torch.optim.Adam does); the parameters then fall into separate launches per
+    (device, dtypes, step), each following the oracle with its own count, and each
+    batch's launch descriptors are built once and reused."""
+    torch.manual_seed(1)
+    a = torch.nn.Parameter(torch.randn(5000, device="cuda") * 0.02)
+    b = torch.nn.Parameter(torch.randn(2048 + 9, device="cuda") * 0.02)
+    c = torch.nn.Parameter((torch.randn(4097, device="cuda") * 0.02).bfloat16())
+    opt = q.Adam8bit([a, b, c], lr=1e-3)
+    refs = {"a": [a.detach().cpu().numpy().copy(), *host_state(a.numel())],
+            "b": [b.detach().cpu().numpy().copy(), *host_state(b.numel())],
+            "c": [to_host(c.detach(), "bf16").copy(), *host_state(c.numel())]}
+    steps = {"a": 0, "b": 0, "c": 0}
+    params = {"a": a, "b": b, "c": c}
+    rng = np.random.default_rng(9)
+    plan = [("a", "b", "c"), ("a",), ("a", "b", "c"), ("a", "c"), ("a", "b", "c")]
+    for it, live in enumerate(plan):
+        for name, p in params.items():
+            p.grad = None
+        for name in live:
+            p = params[name]
+            g = rng.normal(0, 1e-3, p.numel()).astype(np.float32)
+            dt = "bf16" if p.dtype == torch.bfloat16 else "f32"
+            if dt == "bf16":
+                g = oracle.f32_to_bf16_rne(g)
+            p.grad = to_dev(g, dt)
+            steps[name] += 1
+            r = refs[name]
+            refs[name] = list(oracle.adam8bit_step(r[0], g, *r[1:], step=steps[name],
+                                                   param_dtype=dt, grad_dtype=dt, **HP))
+        opt.step()
+        torch.cuda.synchronize()
+        for name, p in params.items():
+            dt = "bf16" if p.dtype == torch.bfloat16 else "f32"
+            what = f"({name}, iteration {it + 1}, step {steps[name]})"
+            assert opt.state[p].get("step", 0) == steps[name], what
+            assert_params(to_host(p.detach(), dt), refs[name][0], dt, 1e-3, what)
+            if steps[name]:
+                st = opt.state[p]
+                assert_state([st[k].cpu().numpy()
+                              for k in ("m_codes", "v_codes", "m_absmax", "v_absmax")],
+                             refs[name][1:], what)
+    # a steady batch reuses its cached launch descriptors
+    for name, p in params.items():
+        p.grad = torch.zeros_like(p)
+    opt.step()
+    cached = dict(opt._prepared)
+    opt.step()
+    assert opt._prepared.keys() == cached.keys()
+    assert all(opt._prepared[k] is cached[k] for k in cached)
+
+
 # ------------------------------------------------------- full-size, sampled
 
 
