@@ -508,13 +508,15 @@ constexpr float kTinyMoment = 0x1p-96f;  // below this, sqrt_rn_unscaled is not 
 // Screen for the bf16 short path.  pf = p - t was computed with a square root and a
 // reciprocal that are each within one ulp (v >= 2^-96 and a normal or zero
 // denominator: every such input was checked on the hardware).  Against the
-// correctly rounded sequence, the relative error of the quotient is below 2^-20.7,
-// so the exact p - t lies within |t| 2^-20 + |pf| 2^-24 of pf (plus 2^-149 where
-// results are subnormal).  c doubles that bound and adds 2^-126; every x in
-// [pf - c, pf + c] therefore covers the exact value, and rounding fp32 -> bf16 is
-// monotone, so if both ends give the same bf16 bits so do the exact value and pf.
+// correctly rounded sequence the quotient's relative error is below 2^-20.6, so t
+// differs from the sequence's t by under |t| 2^-20.3, and after both sides round
+// p - t to binary32 the sequence's result lies within |t| 2^-20.3 + |pf| 2^-23 of pf
+// (plus 2^-149 where results are subnormal).  c takes 2^-19 and 2^-22 for the two
+// factors (2.5 and 2 times the bound) and adds 2^-126; the sequence's result then
+// lies in [pf - c, pf + c], and rounding fp32 -> bf16 is monotone, so if both ends
+// give the same bf16 bits so do that result and pf.
 __device__ __forceinline__ float screen_width(float pf, float t) {
-  return __builtin_fmaf(fabsf(t), 0x1p-18f, __builtin_fmaf(fabsf(pf), 0x1p-20f, 0x1p-126f));
+  return __builtin_fmaf(fabsf(t), 0x1p-19f, __builtin_fmaf(fabsf(pf), 0x1p-22f, 0x1p-126f));
 }
 // Two elements at once: the bf16 bits of both lower ends against both upper ends.
 // A NaN result (0/0 with eps = 0) fails through the unordered test; an infinite

@@ -3,15 +3,18 @@
 For bf16 parameters the kernel may compute p - t with the hardware square root and
 reciprocal (each within one ulp; checked on the hardware over every normal binary32)
 and keep that result only if both ends of [pf - c, pf + c] round to the same bf16
-bits, with c = |t| 2^-18 + |pf| 2^-20 + 2^-126 (each product taken exactly, one
+bits, with c = |t| 2^-19 + |pf| 2^-22 + 2^-126 (each product taken exactly, one
 rounding).  Here the short path is emulated in binary32 with every combination of
 one-ulp errors in the two hardware results, and wherever the screen passes, its bf16
 result must equal the oracle's (the correctly rounded sequence).  The inputs put
 many exact results next to bf16 rounding boundaries (updates as large as the
-parameters), so an unsound width would show.
+parameters), so an unsound width would show: a screen 16 times narrower passes
+wrong results in every case.
 """
 
 import itertools
+import os
+import re
 
 import numpy as np
 import pytest
@@ -19,6 +22,10 @@ import pytest
 import oracle
 
 F32 = np.float32
+# binary exponents of the screen's two factors, as in the kernel's screen_width()
+T_EXP, PF_EXP = -19, -22
+KERNEL_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "block_wise_bit_adam8bit_amd", "csrc", "qopt_kernels.hip")
 
 
 def _ulp_step(x, k):
@@ -56,11 +63,14 @@ def _case(rng, n, lr, beta1, beta2, eps, step):
     return p32, m, v, (eps32, ss, isb), exact32
 
 
-def _screen_and_check(p32, m, v, scalars, exact32):
+def _screen(p32, m, v, scalars, exact32, t_exp=T_EXP, pf_exp=PF_EXP):
+    """Emulated short path and screen over every one-ulp error combination:
+    (number of elements the screen passed with a wrong bf16, elements passed)."""
     eps32, ss, isb = scalars
     want = oracle.f32_to_bf16_rne(exact32)
     usable = (v == 0) | (v >= F32(2.0 ** -96))
     passed_any = np.zeros(p32.size, bool)
+    wrong = 0
     for ds, dr in itertools.product((-1, 0, 1), repeat=2):
         with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
             sq1 = _ulp_step(np.sqrt(v), ds)
@@ -68,33 +78,57 @@ def _screen_and_check(p32, m, v, scalars, exact32):
             r = _ulp_step(F32(1.0) / denom, dr)
             t = ss * (m * r)
             pf = p32 - t
-            c = _fma_down(np.abs(t), 2.0 ** -18, _fma_down(np.abs(pf), 2.0 ** -20,
-                                                            np.full_like(pf, 2.0 ** -126)))
+            c = _fma_down(np.abs(t), 2.0 ** t_exp, _fma_down(np.abs(pf), 2.0 ** pf_exp,
+                                                              np.full_like(pf, 2.0 ** -126)))
             lo, hi = pf - c, pf + c
         ok = usable & ~np.isnan(pf) & (oracle.f32_to_bf16_rne(lo) == oracle.f32_to_bf16_rne(hi))
         got = oracle.f32_to_bf16_rne(pf)
-        bad = np.nonzero(ok & (got != want))[0]
-        assert bad.size == 0, f"screen passed a wrong bf16 at {bad[:5]} (sqrt {ds:+d}, rcp {dr:+d})"
+        wrong += np.count_nonzero(ok & (got != want))
         passed_any |= ok
-    return passed_any
+    return wrong, passed_any
 
 
-@pytest.mark.parametrize("lr,beta1,beta2,eps,step", [
+CASES = [
     (1e-3, 0.9, 0.999, 1e-8, 1),
     (1e-3, 0.9, 0.999, 1e-8, 1000),
     (5e-2, 0.5, 0.75, 1e-6, 3),        # updates as large as the parameters
     (2e-2, 0.9, 0.999, 0.0, 7),
-])
-def test_screen_is_sound(lr, beta1, beta2, eps, step):
+]
+
+
+def _inputs(lr, beta1, beta2, eps, step):
     rng = np.random.default_rng(int(lr * 1e6) + step)
-    n = 1 << 18
-    p32, m, v, scalars, exact32 = _case(rng, n, lr, beta1, beta2, eps, step)
+    return _case(rng, 1 << 18, lr, beta1, beta2, eps, step)
+
+
+@pytest.mark.parametrize("lr,beta1,beta2,eps,step", CASES)
+def test_screen_is_sound(lr, beta1, beta2, eps, step):
+    p32, m, v, scalars, exact32 = _inputs(lr, beta1, beta2, eps, step)
     # exact results within 16 binary32 ulps of a bf16 rounding boundary: the
     # cases an unsound screen would get wrong
     low = exact32.view(np.uint32) & np.uint32(0xFFFF)
     near = np.abs(low.astype(np.int64) - 0x8000) <= 16
     assert np.count_nonzero(near) > 0
-    passed = _screen_and_check(p32, m, v, scalars, exact32)
+    wrong, passed = _screen(p32, m, v, scalars, exact32)
+    assert wrong == 0, f"screen passed {wrong} wrong bf16 results"
     if lr == 1e-3:
         # with ordinary step sizes the short path keeps nearly every element
-        assert np.mean(passed) > 0.99
+        assert np.mean(passed) > 0.999
+
+
+@pytest.mark.parametrize("lr,beta1,beta2,eps,step", CASES)
+def test_narrower_screen_is_caught(lr, beta1, beta2, eps, step):
+    """The cases are sharp enough to expose a screen 16 times narrower than the
+    kernel's (below the error bound): it passes wrong bf16 results."""
+    wrong, _ = _screen(*_inputs(lr, beta1, beta2, eps, step), t_exp=T_EXP - 4,
+                       pf_exp=PF_EXP - 4)
+    assert wrong > 0
+
+
+def test_kernel_uses_the_tested_width():
+    """The exponents tested here are the ones in the kernel's screen_width()."""
+    src = open(KERNEL_SRC).read()
+    body = src[src.index("float screen_width(float pf, float t)"):]
+    body = body[:body.index("}")]
+    exps = [int(e) for e in re.findall(r"0x1p(-?\d+)f", body)]
+    assert exps == [T_EXP, PF_EXP, -126], exps
