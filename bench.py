@@ -47,14 +47,14 @@ def kernel_source_hash():
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
 
 
-def load_traffic(launch_bytes):
+def load_traffic(workload):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    taken on this workload and on the current kernel source; else None."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_hash():
+    if t.get("workload") != workload or t.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return t.get("traffic_bytes_per_launch")
 
@@ -65,6 +65,15 @@ def make_workload(name, torch, workloads):
         shapes, pdt, gdt, seed = workloads.llama7b_shapes(), torch.float32, torch.bfloat16, 3
         label = ("llama7b: 291 tensors, 6,738,415,616 params, fp32 params, bf16 grads "
                  "N(0,1e-3) with 0.01% x1000 outliers, uint8 m/v + fp32 absmax per 2048")
+    elif name == "llama7b_shard8":
+        # one rank's share when 8 ranks split the blocks of the Llama-7B set
+        full = workloads.llama7b_shapes()
+        pieces = workloads.shard_pieces([n for _, n in full], 8, 0)
+        shapes = [(f"{full[i][0]}[{e0}:{e0 + c}]", c) for i, e0, c in pieces]
+        pdt, gdt, seed = torch.float32, torch.bfloat16, 3
+        label = (f"llama7b_shard8: rank 0 of 8 over the blocks of the Llama-7B set, "
+                 f"{len(shapes)} tensor pieces, {sum(c for _, c in shapes):,} params, fp32 "
+                 "params, bf16 grads N(0,1e-3) with 0.01% x1000 outliers")
     elif name == "gpt1p3b":
         shapes, pdt, gdt, seed = workloads.gpt1p3b_shapes(), torch.float32, torch.bfloat16, 2
         label = "gpt1p3b: 243 tensors, 1,311,086,592 params, fp32 params, bf16 grads"
@@ -88,7 +97,7 @@ def make_workload(name, torch, workloads):
         G[:rows * dim].view(rows, dim)[~mask] = 0
     else:
         workloads.fill_normal_(G, 1e-3, seed * 1000 + 1)
-        if name == "llama7b":
+        if name in ("llama7b", "llama7b_shard8"):
             workloads.scale_random_entries_(G, 1e-4, 1000.0, seed * 1000 + 1)
     tensors, off = [], 0
     for n in sizes:
@@ -108,12 +117,10 @@ def cpu_baseline(target_seconds=12.0):
     import workloads
 
     n = 2048 * 2048
-    rng = np.random.default_rng(3)
     p = workloads.host_normal(n, 0.02, 31)
     g = oracle.f32_to_bf16_rne(workloads.host_normal(n, 1e-3, 32))
     st = [np.zeros(n, np.uint8), np.zeros(n, np.uint8), np.zeros(2048, np.float32),
           np.zeros(2048, np.float32)]
-    del rng
     steps, t0 = 0, time.perf_counter()
     while True:
         out = oracle.adam8bit_step(p, g, *st, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
@@ -391,8 +398,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b",
-                    choices=["llama7b", "gpt1p3b", "flat20b", "codec256m", "convert7b",
-                             "embed7b"])
+                    choices=["llama7b", "llama7b_shard8", "gpt1p3b", "flat20b", "codec256m",
+                             "convert7b", "embed7b"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hbm-reference", action="store_true",
                     help="only time torch's copy_, fill_ and sum over 8 GiB buffers")
@@ -470,7 +477,7 @@ def main():
     achieved = launch_bytes / avg_launch_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic(launch_bytes),
+                "traffic": load_traffic(args.workload),
                 "kernel": "adam8bit_kernel", "launches_per_step": launches,
                 "avg_launch_ms": round(avg_launch_s * 1e3, 4),
                 "algorithmic_bytes_per_launch": int(launch_bytes)}

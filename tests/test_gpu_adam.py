@@ -185,6 +185,42 @@ def test_misaligned_views(q):
     run_small(q, sizes, "f32", "f32", steps=3, seed=5, views=views)
 
 
+@pytest.mark.parametrize("pdt,gdt", [("f32", "bf16"), ("bf16", "bf16")])
+def test_rank_shares_step_independently(q, pdt, gdt):
+    """Three ranks' shares (contiguous ranges of whole blocks of the flattened tensors,
+    each stepped by its own call on views of the full tensors and block maxima) give
+    the oracle's whole-tensor step, element for element."""
+    sizes = [5 * 2048 + 5, 2048, 5000, 9 * 2048, 1, 2049, 4 * 2048 + 100]
+    world = 3
+    rng = np.random.default_rng(21)
+    hp_p = [host_params(n, pdt, rng) for n in sizes]
+    hs = [host_state(n) for n in sizes]
+    dp = [to_dev(p, pdt) for p in hp_p]
+    ds = [dev_state(n) for n in sizes]
+    shares = [workloads.shard_pieces(sizes, world, r) for r in range(world)]
+    # tensors 2 and 3 are split between ranks, one piece being tensor 2's ragged tail
+    assert (2, 4096, 904) in shares[1] and sum(len(s) for s in shares) == len(sizes) + 2
+    for step in range(1, 4):
+        hg = [host_grads(n, gdt, rng) for n in sizes]
+        dg = [to_dev(g, gdt) for g in hg]
+        for r, pieces in enumerate(shares):
+            items = []
+            for i, e0, c in pieces:
+                b0, nb = e0 // BLOCK, -(-c // BLOCK)
+                items.append((dp[i][e0:e0 + c], dg[i][e0:e0 + c], ds[i][0][e0:e0 + c],
+                              ds[i][1][e0:e0 + c], ds[i][2][b0:b0 + nb], ds[i][3][b0:b0 + nb]))
+            q.qopt_adam8bit_step(items, step=step, **HP)
+        for i in range(len(sizes)):
+            out = oracle.adam8bit_step(hp_p[i], hg[i], *hs[i], step=step, param_dtype=pdt,
+                                       grad_dtype=gdt, **HP)
+            hp_p[i], hs[i] = out[0], list(out[1:])
+        torch.cuda.synchronize()
+        for i, n in enumerate(sizes):
+            what = f"(tensor {i}, n={n}, step {step}, {world} shares, {pdt}/{gdt})"
+            assert_state([t.cpu().numpy() for t in ds[i]], hs[i], what)
+            assert_params(to_host(dp[i], pdt), hp_p[i], pdt, HP["lr"], what)
+
+
 def _grads_max_at_position(n, gdt, rng):
     """Block b's largest gradient sits at element b % 2048 of the block (signs
     alternating), so over 2048 blocks the largest m and v of a block are held once

@@ -23,6 +23,10 @@ not throughput workloads):
                  g ~ N(0, 5e-4); the first 256,000 x 4096 elements form an embedding
                  whose gradient rows are nonzero in 2 % of the rows (5,120 rows drawn
                  per step), zero elsewhere in that region.
+* ``llama7b_shard8``  one rank's share of ``llama7b`` when 8 ranks split the 2048-blocks
+                 of the flattened parameter set into contiguous ranges (rank 0: the
+                 first 411,281 blocks, 842,303,488 params in 35 tensor pieces); same
+                 value recipe and seed as ``llama7b``.
 * ``embed7b``    the Stable Embedding layer at the Llama-7B embedding's shape: a
                  32,000 x 4096 table, 65,536 tokens (32 sequences of 2048) whose ids
                  follow Zipf's law with exponent 1 over the vocabulary (ranks mapped
@@ -75,6 +79,29 @@ HPARAMS = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
 
 def nblocks(n):
     return -(-int(n) // BLOCK)
+
+
+def shard_pieces(sizes, world, rank):
+    """Rank ``rank``'s share when ``world`` ranks split the 2048-blocks of the
+    flattened tensors (blocks counted per tensor, the last one of a tensor may be
+    short) into contiguous ranges, the first ``total % world`` ranks one block
+    longer: a list of (tensor index, first element, element count), every first
+    element a multiple of 2048 within its tensor."""
+    if not 0 <= rank < world:
+        raise ValueError(f"rank {rank} outside 0..{world - 1}")
+    nbs = [nblocks(n) for n in sizes]
+    total = sum(nbs)
+    per, extra = divmod(total, world)
+    lo = rank * per + min(rank, extra)
+    hi = lo + per + (1 if rank < extra else 0)
+    out, first = [], 0                    # first: global index of the tensor's block 0
+    for i, (n, nb) in enumerate(zip(sizes, nbs)):
+        a, b = max(lo, first), min(hi, first + nb)
+        if a < b:
+            e0 = (a - first) * BLOCK
+            out.append((i, e0, min(int(n), (b - first) * BLOCK) - e0))
+        first += nb
+    return out
 
 
 # ---------------------------------------------------------------------- host (numpy)
