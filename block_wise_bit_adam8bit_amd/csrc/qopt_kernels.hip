@@ -425,8 +425,16 @@ dequantize_kernel(CodecChunk c, const qopt_codebook* cb_g) {
 
 struct AdamScalars {
   float b1, b2, omb1, omb2, eps, step_size, inv_sqrt_bc2;
-  uint32_t bf16_screen;  // 1: bf16 parameters may take the screened short path
+  // the screened short path for bf16 parameters: its denominator is
+  // sqrt(v) * short_a + short_b = (sqrt(v) * inv_sqrt_bc2 + eps) / step_size, so that
+  // t = m / denominator; it is taken only where |t| < t_limit
+  float short_a, short_b, t_limit;
 };
+
+// How bf16 parameters use the screened short path (fp32 parameters never do):
+// not at all, or screened, or screened with slices holding a subnormal second
+// moment sent to the correctly rounded sequence as well.
+enum ScreenMode : int { kNoScreen = 0, kScreen = 1, kScreenSubCheck = 2 };
 
 // One launch's work: up to kMaxTensors pieces, each a run of whole blocks of one
 // tensor.  Large tensors may be split over several launches so that every launch
@@ -505,29 +513,37 @@ __device__ __forceinline__ float sqrt_rn_unscaled(float x) {
 
 constexpr float kTinyMoment = 0x1p-96f;  // below this, sqrt_rn_unscaled is not exact
 
-// Screen for the bf16 short path.  pf = p - t was computed with a square root and a
-// reciprocal that are each within one ulp (v >= 2^-96 and a normal or zero
-// denominator: every such input was checked on the hardware).  Against the
-// correctly rounded sequence the quotient's relative error is below 2^-20.6, so t
-// differs from the sequence's t by under |t| 2^-20.3, and after both sides round
-// p - t to binary32 the sequence's result lies within |t| 2^-20.3 + |pf| 2^-23 of pf
-// (plus 2^-149 where results are subnormal).  c takes 2^-19 and 2^-22 for the two
-// factors (2.5 and 2 times the bound) and adds 2^-126; the sequence's result then
-// lies in [pf - c, pf + c], and rounding fp32 -> bf16 is monotone, so if both ends
-// give the same bf16 bits so do that result and pf.
+// Screen for the bf16 short path.  There t = m * rcp(fma(sq, a, b)) with sq the
+// hardware square root of a normal or zero v and a, b the step's scalars folded as
+// in AdamScalars.  The hardware square root and reciprocal are each within one ulp
+// on those inputs (every normal square-root input, and every normal reciprocal input
+// up to 2^126, was checked on the hardware; subnormal square-root inputs flush to
+// zero, so they never reach this path).  In units of 2^-24, t is then within 7 of
+// the exact m / ((sqrt(v) inv_sqrt_bc2 + eps) / step_size) (square root 2, a 1, the
+// fma 1, reciprocal 2, product 1; b's 1 does not add), and the correctly rounded
+// sequence's t within 5 of it: they differ by under |t| 2^-20.3.  After both sides
+// round p - t to binary32 the sequence's result lies within |t| 2^-20.3 + |pf| 2^-23
+// of pf (plus 2^-149 where results are subnormal).  c takes 2^-19 and 2^-22 for the
+// two factors (2.5 and 2 times the bound) and adds 2^-126; the sequence's result
+// then lies in [pf - c, pf + c], and rounding fp32 -> bf16 is monotone, so if both
+// ends give the same bf16 bits so do that result and pf.
 __device__ __forceinline__ float screen_width(float pf, float t) {
   return __builtin_fmaf(fabsf(t), 0x1p-19f, __builtin_fmaf(fabsf(pf), 0x1p-22f, 0x1p-126f));
 }
-// Two elements at once: the bf16 bits of both lower ends against both upper ends.
-// A NaN result (0/0 with eps = 0) fails through the unordered test; an infinite
-// one makes one end NaN and the other infinite, which differ.
-__device__ __forceinline__ uint32_t screen_bf16x2(float pf0, float t0, float pf1, float t1) {
+// Two elements at once: true where the bf16 bits of the lower ends differ from
+// those of the upper ends.  An infinite pf makes one end NaN and the other
+// infinite, which differ; a NaN t is caught by the bound on |t| that goes with this
+// screen (see update_vec).
+__device__ __forceinline__ bool screen_fails_bf16x2(float pf0, float t0, float pf1, float t1) {
   const float c0 = screen_width(pf0, t0);
   const float c1 = screen_width(pf1, t1);
   const uint32_t lo = pack_bf16x2(pf0 - c0, pf1 - c1);
   const uint32_t hi = pack_bf16x2(pf0 + c0, pf1 + c1);
-  return (lo ^ hi) | static_cast<uint32_t>(__builtin_isunordered(pf0, pf1));
+  return lo != hi;
 }
+
+// Positive subnormal, as a __builtin_amdgcn_classf mask.
+constexpr int kClassPosSubnormal = 0x80;
 
 // Where one block lives, resolved from the launch's piece table (wave-uniform).
 struct BlockRef {
@@ -615,7 +631,7 @@ __device__ __forceinline__ void unstash_v(const float* vstash, int s, int lane, 
 
 // Update of a full block from prefetched vector inputs; stores p, keeps m and v
 // (v in the LDS stash where StepShape says so).
-template <typename PT, typename GT>
+template <typename PT, typename GT, int kMode>
 __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_codebook& cbm,
                                            const qopt_codebook& cbv, const BlockIn<PT, GT>& in,
                                            const BlockRef& r, int lane, float m[kSlices][4],
@@ -628,6 +644,7 @@ __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_code
     float p4[4], g4[4];
     unpack4(in.p[s], p4);
     unpack4(in.g[s], g4);
+    constexpr bool kScreened = std::is_same<PT, uint16_t>::value && kMode != kNoScreen;
     // the moments of the slice's 4 elements, then their square roots: the short
     // sequence unless some lane of the wave holds a tiny second moment
     uint64_t tiny = 0;  // lanes (as a wave mask) holding 0 < v < 2^-96
@@ -637,33 +654,55 @@ __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_code
       const float v_prev = cbv.decode[(in.cv[s] >> (8 * j)) & 0xFFu] * in.av;
       m[s][j] = (k.b1 * m_prev) + (k.omb1 * g4[j]);
       v[s][j] = (k.b2 * v_prev) + (k.omb2 * (g4[j] * g4[j]));
-      // 0 < v < 2^-96 as one unsigned compare on the bits (v is never negative)
-      tiny |= __builtin_amdgcn_ballot_w64((__float_as_uint(v[s][j]) - 1u) <
-                                          (__float_as_uint(kTinyMoment) - 1u));
+      // 0 < v < 2^-96 as one unsigned compare on the bits (v is never negative);
+      // bf16 parameters take it only on their fallback below
+      if constexpr (!kScreened)
+        tiny |= __builtin_amdgcn_ballot_w64((__float_as_uint(v[s][j]) - 1u) <
+                                            (__float_as_uint(kTinyMoment) - 1u));
     }
     bool exact = true;
-    if constexpr (std::is_same<PT, uint16_t>::value) {
+    if constexpr (kScreened) {
       // bf16 parameters: the short path (hardware square root and reciprocal, each
       // within one ulp on the inputs that reach it) gives the same bf16 result as
       // the correctly rounded sequence whenever its fp32 result is far enough from
-      // a bf16 rounding boundary; lanes where it is not fall back below.
-      if (tiny == 0 && k.bf16_screen) {
+      // a bf16 rounding boundary; lanes where it is not fall back below.  The
+      // hardware square root flushes subnormal second moments to zero; unless eps
+      // makes that harmless (kMode kScreen), such slices fall back as well.
+      uint64_t sub = 0;
+      if constexpr (kMode == kScreenSubCheck)
+        sub = __builtin_amdgcn_ballot_w64(__builtin_amdgcn_classf(v[s][0], kClassPosSubnormal) |
+                                          __builtin_amdgcn_classf(v[s][1], kClassPosSubnormal) |
+                                          __builtin_amdgcn_classf(v[s][2], kClassPosSubnormal) |
+                                          __builtin_amdgcn_classf(v[s][3], kClassPosSubnormal));
+      if (sub == 0) {
         float pf[4], t[4];
+        // The short path never forms m / denominator, which the sequence rounds on
+        // its own and which may overflow where t does not; where |t| < t_limit
+        // (min(step_size, 1) 2^127) neither the sequence's quotient nor its t can
+        // overflow.  A NaN t (0/0 with eps = 0) fails the compare too.
+        uint64_t unbounded = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float sq1 = __builtin_amdgcn_sqrtf(v[s][j]);
-          const float denom = (sq1 * k.inv_sqrt_bc2) + k.eps;
-          const float u = m[s][j] * __builtin_amdgcn_rcpf(denom);
-          t[j] = k.step_size * u;
+          const float denom = __builtin_fmaf(sq1, k.short_a, k.short_b);
+          t[j] = m[s][j] * __builtin_amdgcn_rcpf(denom);
           pf[j] = p4[j] - t[j];
+          unbounded |= __builtin_amdgcn_ballot_w64(!(fabsf(t[j]) < k.t_limit));
         }
-        const uint32_t unsafe = screen_bf16x2(pf[0], t[0], pf[1], t[1]) |
-                                screen_bf16x2(pf[2], t[2], pf[3], t[3]);
-        if (__builtin_amdgcn_ballot_w64(unsafe != 0) == 0) {
+        const uint64_t unsafe =
+            unbounded | __builtin_amdgcn_ballot_w64(screen_fails_bf16x2(pf[0], t[0], pf[1], t[1])) |
+            __builtin_amdgcn_ballot_w64(screen_fails_bf16x2(pf[2], t[2], pf[3], t[3]));
+        if (unsafe == 0) {
           exact = false;
 #pragma unroll
           for (int j = 0; j < 4; ++j) p4[j] = pf[j];
         }
+      }
+      if (exact) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          tiny |= __builtin_amdgcn_ballot_w64((__float_as_uint(v[s][j]) - 1u) <
+                                              (__float_as_uint(kTinyMoment) - 1u));
       }
     }
     if (exact) {
@@ -778,7 +817,7 @@ __device__ __forceinline__ void requantize(const Encoder& em, const Encoder& ev,
 // the vector inputs of its next block are already in flight (loaded into the
 // registers the update no longer needs), so memory stays busy through the
 // requantization phase.
-template <typename PT, typename GT>
+template <typename PT, typename GT, int kMode>
 __global__ void __launch_bounds__(kThreads, StepShape<PT>::kWavesPerSimd)
 adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qopt_codebook* cbv_g) {
   constexpr bool kVInLds = StepShape<PT>::kVInLds;
@@ -806,7 +845,7 @@ adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qo
     float m[kSlices][4], v[kSlices][4];
     float mmax = 0.0f, vmax = 0.0f;
     if (cur.vec)
-      update_vec(k, cb[0], cb[1], in, cur, lane, m, v, vstash, mmax, vmax);
+      update_vec<PT, GT, kMode>(k, cb[0], cb[1], in, cur, lane, m, v, vstash, mmax, vmax);
     else
       update_scalar<PT, GT>(k, cb[0], cb[1], cur, lane, m, v, vstash, mmax, vmax);
     // The stash must really go through LDS: without this the compiler may forward
@@ -1027,12 +1066,28 @@ struct CodecSize {
   int64_t operator()(int32_t i) const { return t[i].n; }
 };
 
+template <typename PT, typename GT, int kMode>
+int launch_step_mode(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size_t gsize,
+                     const AdamScalars& k, const qopt_codebook* cbm, const qopt_codebook* cbv,
+                     hipStream_t stream) {
+  return launch_planned<StepChunk>(adam8bit_kernel<PT, GT, kMode>, 0, kStepRun, ntensors,
+                                   StepSize{tensors}, StepFill{tensors, psize, gsize}, stream, k,
+                                   cbm, cbv);
+}
+
+// mode: a ScreenMode, which only bf16 parameters use.
 template <typename PT, typename GT>
 int launch_step_chunks(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size_t gsize,
-                       const AdamScalars& k, const qopt_codebook* cbm, const qopt_codebook* cbv,
-                       hipStream_t stream) {
-  return launch_planned<StepChunk>(adam8bit_kernel<PT, GT>, 0, kStepRun, ntensors, StepSize{tensors},
-                                   StepFill{tensors, psize, gsize}, stream, k, cbm, cbv);
+                       const AdamScalars& k, int mode, const qopt_codebook* cbm,
+                       const qopt_codebook* cbv, hipStream_t stream) {
+  if constexpr (std::is_same<PT, uint16_t>::value) {
+    if (mode == kScreen)
+      return launch_step_mode<PT, GT, kScreen>(tensors, ntensors, psize, gsize, k, cbm, cbv, stream);
+    if (mode == kScreenSubCheck)
+      return launch_step_mode<PT, GT, kScreenSubCheck>(tensors, ntensors, psize, gsize, k, cbm, cbv,
+                                                       stream);
+  }
+  return launch_step_mode<PT, GT, kNoScreen>(tensors, ntensors, psize, gsize, k, cbm, cbv, stream);
 }
 
 int check_step_tensors(const qopt_tensor* tensors, int32_t ntensors, int param_dtype,
@@ -1166,21 +1221,43 @@ extern "C" int qopt_adam8bit_step(const qopt_tensor* tensors, int32_t ntensors, 
   const double bc2 = 1.0 - pow_by_squaring(static_cast<double>(hp->beta2), hp->step);
   k.step_size = static_cast<float>(static_cast<double>(hp->lr) / bc1);
   k.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(bc2));
-  // The screen's error bound needs a normal (or zero) denominator in front of the
-  // hardware reciprocal, whose accuracy was only established on normal inputs, so
-  // no subnormal eps; and a step size below 2^20, so that subnormal rounding errors
-  // scaled by it stay under the bound's 2^-126 floor.
-  k.bf16_screen =
-      ((hp->eps == 0.0f || hp->eps >= 0x1p-126f) && k.step_size <= 0x1p20f) ? 1u : 0u;
+  // The bf16 short path's folded scalars, each one rounding of an exact quotient of
+  // binary32 values.  Its error bound needs a and b normal (or b zero) and a
+  // denominator fma(sq, a, b) that is normal, zero or infinite and at most 2^126
+  // when finite (the range where the hardware reciprocal was checked): sq is 0, in
+  // [2^-63, 2^64] or infinite, hence a in [2^-63, 2^61] and b at most 2^125.  The
+  // step size must be positive and at most 2^20, so that subnormal rounding errors
+  // of the sequence's quotient, scaled by it, stay under the bound's 2^-126 floor.
+  const double ss = static_cast<double>(k.step_size);
+  k.short_a = ss > 0.0 ? static_cast<float>(static_cast<double>(k.inv_sqrt_bc2) / ss) : 0.0f;
+  k.short_b = ss > 0.0 ? static_cast<float>(static_cast<double>(k.eps) / ss) : 0.0f;
+  k.t_limit = static_cast<float>((ss < 1.0 ? ss : 1.0) * 0x1p127);
+  const bool a_ok = k.short_a >= 0x1p-63f && k.short_a <= 0x1p61f;
+  const bool b_ok = k.short_b == 0.0f || (k.short_b >= 0x1p-126f && k.short_b <= 0x1p125f);
+  const bool screen = ss > 0.0 && ss <= 0x1p20 && a_ok && b_ok;
+  // A subnormal v (below 2^-126) has a square root below 2^-63, which the hardware
+  // flushes to zero.  With eps >= 2^-39 inv_sqrt_bc2 (so a / b <= 2^39, up to the two
+  // roundings of a and b) that moves the denominator by under 2^-63 a / b, about
+  // 2^-24 of itself, inside the 2^-23 the error bound allows for the square root.
+  // With eps = 0 it makes the denominator 0 and t infinite or NaN, which the bound on
+  // |t| rejects.  Only eps in between needs a test for subnormal v.
+  const bool sub_check =
+      k.eps != 0.0f &&
+      !(static_cast<double>(k.eps) >= static_cast<double>(k.inv_sqrt_bc2) * 0x1p-39);
+  const int mode = !screen ? kNoScreen : (sub_check ? kScreenSubCheck : kScreen);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (param_dtype == QOPT_F32 && grad_dtype == QOPT_F32)
-    return launch_step_chunks<float, float>(tensors, ntensors, psize, gsize, k, cb_m_dev, cb_v_dev, s);
+    return launch_step_chunks<float, float>(tensors, ntensors, psize, gsize, k, mode, cb_m_dev,
+                                            cb_v_dev, s);
   if (param_dtype == QOPT_F32 && grad_dtype == QOPT_BF16)
-    return launch_step_chunks<float, uint16_t>(tensors, ntensors, psize, gsize, k, cb_m_dev, cb_v_dev, s);
+    return launch_step_chunks<float, uint16_t>(tensors, ntensors, psize, gsize, k, mode, cb_m_dev,
+                                               cb_v_dev, s);
   if (param_dtype == QOPT_BF16 && grad_dtype == QOPT_F32)
-    return launch_step_chunks<uint16_t, float>(tensors, ntensors, psize, gsize, k, cb_m_dev, cb_v_dev, s);
-  return launch_step_chunks<uint16_t, uint16_t>(tensors, ntensors, psize, gsize, k, cb_m_dev, cb_v_dev, s);
+    return launch_step_chunks<uint16_t, float>(tensors, ntensors, psize, gsize, k, mode, cb_m_dev,
+                                               cb_v_dev, s);
+  return launch_step_chunks<uint16_t, uint16_t>(tensors, ntensors, psize, gsize, k, mode, cb_m_dev,
+                                                  cb_v_dev, s);
 }
 
 extern "C" int qopt_adam8bit_launch_count(const qopt_tensor* tensors, int32_t ntensors,

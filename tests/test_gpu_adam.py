@@ -280,6 +280,66 @@ def test_bf16_params_short_path(q, hp, gdt):
     run_small(q, [2 ** 19 + 333], "bf16", gdt, steps=3, seed=12, hp=hp)
 
 
+def step_from_state(q, p, g, cm, cv, am, av, pdt, gdt, step, hp):
+    """One kernel step from the given host state against the oracle's, every element."""
+    dp, dg = to_dev(p, pdt), to_dev(g, gdt)
+    ds = [torch.from_numpy(x.copy()).cuda() for x in (cm, cv, am, av)]
+    q.qopt_adam8bit_step([(dp, dg, *ds)], step=step, **hp)
+    ref = oracle.adam8bit_step(p, g, cm, cv, am, av, step=step, param_dtype=pdt,
+                               grad_dtype=gdt, **hp)
+    torch.cuda.synchronize()
+    what = f"({pdt}/{gdt}, step {step}, {hp})"
+    assert_state([t.cpu().numpy() for t in ds], list(ref[1:]), what)
+    assert_params(to_host(dp, pdt), ref[0], pdt, hp["lr"], what)
+    return ref[0]
+
+
+@pytest.mark.parametrize("gdt", ["bf16", "f32"])
+def test_bf16_quotient_overflow(q, gdt):
+    """Large first moments over small second moments with eps = 0: m / denominator
+    overflows binary32 for part of the elements (the sequence's parameter becomes
+    infinite) while step_size * m / denominator does not.  The bf16 short path never
+    forms that quotient; its bound on |t| must send those slices to the sequence."""
+    rng = np.random.default_rng(31)
+    n = 16 * 2048
+    p = oracle.f32_to_bf16_rne(rng.normal(0, 1.0, n).astype(np.float32))
+    g = np.zeros(n, np.float32)
+    g = oracle.f32_to_bf16_rne(g) if gdt == "bf16" else g
+    cm = rng.integers(0, 256, n).astype(np.uint8)
+    cv = rng.integers(1, 256, n).astype(np.uint8)
+    am = np.full(16, 1e30, np.float32)
+    av = (10.0 ** rng.uniform(-22, -16, 16)).astype(np.float32)
+    say(f"bf16 quotient overflow grads {gdt}")
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        ref = step_from_state(q, p, g, cm, cv, am, av, "bf16", gdt, 1000,
+                              dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=0.0))
+    inf = np.count_nonzero((ref & 0x7FFF) == 0x7F80)
+    assert 100 < inf < n - 100
+
+
+@pytest.mark.parametrize("eps", [1e-30, 1e-8, 0.0])
+def test_bf16_subnormal_second_moments(q, eps):
+    """Second moments spread over the subnormals and the smallest normals.  The
+    hardware square root flushes subnormal inputs to zero: with eps = 1e-30 the
+    kernel checks every slice for them, with eps = 1e-8 (large enough) and eps = 0
+    (denominator 0, t rejected by its bound) it does not, and all three must give the
+    oracle's bits."""
+    rng = np.random.default_rng(33)
+    n = 16 * 2048 + 5
+    nb = -(-n // BLOCK)
+    p = oracle.f32_to_bf16_rne(rng.normal(0, 0.02, n).astype(np.float32))
+    g = (rng.choice([-1.0, 1.0], n) * 10.0 ** rng.uniform(-24, -18, n)).astype(np.float32)
+    g = oracle.f32_to_bf16_rne(g)
+    cm = rng.integers(0, 256, n).astype(np.uint8)
+    cv = rng.integers(0, 256, n).astype(np.uint8)
+    am = (10.0 ** rng.uniform(-9, -6, nb)).astype(np.float32)
+    av = (10.0 ** rng.uniform(-44, -36, nb)).astype(np.float32)
+    say(f"bf16 subnormal second moments eps={eps}")
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        step_from_state(q, p, g, cm, cv, am, av, "bf16", "bf16", 3,
+                        dict(lr=5e-2, beta1=0.5, beta2=0.75, eps=eps))
+
+
 def test_late_step_and_zero_blocks(q):
     """A large step number, and blocks whose gradient and state are zero."""
     n = 4 * 2048
