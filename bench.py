@@ -59,8 +59,13 @@ def load_traffic(workload):
     return t.get("traffic_bytes_per_launch")
 
 
-def make_workload(name, torch, workloads):
-    """Device tensors of the workload: (tensors, sizes, pdtype, gdtype, label)."""
+def make_workload(name, torch, workloads, layout="flat"):
+    """Device tensors of the workload: (tensors, sizes, pdtype, gdtype, label).
+
+    layout "flat": parameters, gradients and each kind of optimizer state in one
+    buffer each, every tensor a view (flattened parameters, as sharded data-parallel
+    training keeps them).  layout "params": one allocation per parameter and per
+    gradient, as a model holds them, with the state as Adam8bit allocates it."""
     if name == "llama7b":
         shapes, pdt, gdt, seed = workloads.llama7b_shapes(), torch.float32, torch.bfloat16, 3
         label = ("llama7b: 291 tensors, 6,738,415,616 params, fp32 params, bf16 grads "
@@ -85,6 +90,20 @@ def make_workload(name, torch, workloads):
     sizes = [n for _, n in shapes]
     total = sum(sizes)
     dev = torch.device("cuda", 0)
+    if layout == "params":
+        from block_wise_bit_adam8bit_amd.optim import _flat_state
+        tensors = []
+        for i, n in enumerate(sizes):
+            p = torch.empty(n, dtype=pdt, device=dev)
+            g = torch.empty(n, dtype=gdt, device=dev)
+            workloads.fill_normal_(p, 0.02, seed * 100000 + i)
+            workloads.fill_normal_(g, 1e-3, seed * 100000 + 50000 + i)
+            if name in ("llama7b", "llama7b_shard8"):
+                workloads.scale_random_entries_(g, 1e-4, 1000.0, seed * 100000 + 90000 + i)
+            tensors.append((p, g))
+        states = _flat_state(dev, sizes)
+        tensors = [(p, g, *st) for (p, g), st in zip(tensors, states)]
+        return tensors, sizes, pdt, gdt, label + "; one allocation per parameter and gradient"
     P = torch.empty(total, dtype=pdt, device=dev)
     G = torch.empty(total, dtype=gdt, device=dev)
     CM = torch.zeros(total, dtype=torch.uint8, device=dev)
@@ -400,6 +419,9 @@ def main():
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "llama7b_shard8", "gpt1p3b", "flat20b", "codec256m",
                              "convert7b", "embed7b"])
+    ap.add_argument("--layout", default="flat", choices=["flat", "params"],
+                    help="flat buffers with views (default), or one allocation per parameter "
+                         "and gradient (llama7b, llama7b_shard8, gpt1p3b)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hbm-reference", action="store_true",
                     help="only time torch's copy_, fill_ and sum over 8 GiB buffers")
@@ -434,7 +456,9 @@ def main():
     if args.workload == "embed7b":
         return bench_embed(torch, workloads, q, args)
     log(f"building workload {args.workload}")
-    tensors, sizes, pdt, gdt, label = make_workload(args.workload, torch, workloads)
+    if args.layout != "flat" and args.workload == "flat20b":
+        raise SystemExit("--layout params takes a workload made of several parameters")
+    tensors, sizes, pdt, gdt, label = make_workload(args.workload, torch, workloads, args.layout)
     prepared = q.make_tensor_array(tensors)
     launches = q.qopt_adam8bit_launch_count(tensors, _prepared=prepared)
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
@@ -477,7 +501,7 @@ def main():
     achieved = launch_bytes / avg_launch_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic(args.workload),
+                "traffic": load_traffic(args.workload) if args.layout == "flat" else None,
                 "kernel": "adam8bit_kernel", "launches_per_step": launches,
                 "avg_launch_ms": round(avg_launch_s * 1e3, 4),
                 "algorithmic_bytes_per_launch": int(launch_bytes)}
@@ -502,7 +526,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if pdt == torch.float32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": label, "params": nparams, "tensors": len(sizes),
+        "config": {"workload": label, "layout": args.layout, "params": nparams,
+                   "tensors": len(sizes),
                    "bytes_per_param": round(step_bytes / nparams, 4),
                    "algorithmic_bytes_per_step": step_bytes, "parallelism": "single GPU"},
         "roofline": roofline,
