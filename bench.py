@@ -414,8 +414,8 @@ def bench_embed(torch, workloads, q, args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama7b",
                     choices=["llama7b", "llama7b_shard8", "gpt1p3b", "flat20b", "codec256m",
                              "convert7b", "embed7b"])
@@ -481,18 +481,19 @@ def main():
         one_step()
     torch.cuda.synchronize()
 
+    # one event per step boundary, on the stream the kernels run on
     stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    events[0].record(stream)
+    for i in range(args.steps):
         one_step()
-    ev1.record(stream)
+        events[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1)
+    ev_ms = events[0].elapsed_time(events[-1])
+    step_ms = sorted(events[i].elapsed_time(events[i + 1]) for i in range(args.steps))
     ms_per_step = wall * 1e3 / args.steps
     log(f"timed: wall {wall:.4f} s, events {ev_ms:.3f} ms")
 
@@ -504,6 +505,8 @@ def main():
                 "traffic": load_traffic(args.workload) if args.layout == "flat" else None,
                 "kernel": "adam8bit_kernel", "launches_per_step": launches,
                 "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                "step_ms_median": round(step_ms[len(step_ms) // 2], 4),
+                "step_ms_min": round(step_ms[0], 4),
                 "algorithmic_bytes_per_launch": int(launch_bytes)}
 
     cpu = None
