@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -43,18 +44,24 @@ def algorithmic_bytes(sizes, pbytes, gbytes):
     return total
 
 
-def kernel_source_hash():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+def kernel_code_hash(text=None):
+    """sha256 of the step kernel's source with comments removed and whitespace
+    collapsed: it changes with the code, not with its comments."""
+    if text is None:
+        text = open(KERNEL_SRC).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()
 
 
 def load_traffic(workload):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they were
-    taken on this workload and on the current kernel source; else None."""
+    taken on this workload and on the current kernel code; else None."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("workload") != workload or t.get("kernel_source_sha256") != kernel_source_hash():
+    if t.get("workload") != workload or t.get("kernel_code_sha256") != kernel_code_hash():
         return None
     return t.get("traffic_bytes_per_launch")
 

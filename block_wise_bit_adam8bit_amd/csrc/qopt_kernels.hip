@@ -645,8 +645,9 @@ __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_code
     unpack4(in.p[s], p4);
     unpack4(in.g[s], g4);
     constexpr bool kScreened = std::is_same<PT, uint16_t>::value && kMode != kNoScreen;
-    // the moments of the slice's 4 elements, then their square roots: the short
-    // sequence unless some lane of the wave holds a tiny second moment
+    // the moments of the slice's 4 elements; where the correctly rounded sequence
+    // runs, its square roots skip sqrtf's rescaling of tiny inputs unless some lane of
+    // the wave holds a tiny second moment
     uint64_t tiny = 0;  // lanes (as a wave mask) holding 0 < v < 2^-96
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

@@ -9,7 +9,6 @@ CPU tests cover:
 The GPU test runs a short bench and checks every key of its JSON line.
 """
 
-import hashlib
 import json
 import os
 import subprocess
@@ -39,19 +38,28 @@ def test_algorithmic_bytes():
     assert bench.algorithmic_bytes([], 4, 2) == 0
 
 
+def test_kernel_code_hash_ignores_comments_only():
+    src = open(bench.KERNEL_SRC).read()
+    h = bench.kernel_code_hash()
+    assert h == bench.kernel_code_hash(src)
+    assert bench.kernel_code_hash("// a note\n" + src.replace("\n", "\n  ") + "\n/* more */") == h
+    # a changed constant in the code is a changed kernel
+    assert bench.kernel_code_hash(src.replace("0x1p-19f", "0x1p-20f")) != h
+    assert bench.kernel_code_hash(src.replace("kStepRun = 2", "kStepRun = 4")) != h
+
+
 def test_traffic_file_guards(tmp_path, monkeypatch):
-    sha = bench.kernel_source_hash()
-    assert sha == hashlib.sha256(open(bench.KERNEL_SRC, "rb").read()).hexdigest()
+    sha = bench.kernel_code_hash()
     path = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
     assert bench.load_traffic("llama7b") is None                      # no file
     path.write_text("not json")
     assert bench.load_traffic("llama7b") is None
-    good = {"workload": "llama7b", "kernel_source_sha256": sha, "traffic_bytes_per_launch": 123}
+    good = {"workload": "llama7b", "kernel_code_sha256": sha, "traffic_bytes_per_launch": 123}
     path.write_text(json.dumps(good))
     assert bench.load_traffic("llama7b") == 123
     assert bench.load_traffic("gpt1p3b") is None                      # other workload
-    path.write_text(json.dumps(dict(good, kernel_source_sha256="0" * 64)))
+    path.write_text(json.dumps(dict(good, kernel_code_sha256="0" * 64)))
     assert bench.load_traffic("llama7b") is None                      # kernel changed since
 
 
