@@ -340,6 +340,44 @@ def test_bf16_subnormal_second_moments(q, eps):
                         dict(lr=5e-2, beta1=0.5, beta2=0.75, eps=eps))
 
 
+@pytest.mark.parametrize("pdt,gdt", [("f32", "bf16"), ("bf16", "bf16"), ("f32", "f32")])
+def test_non_finite_gradients_stay_in_their_blocks(q, pdt, gdt):
+    """Non-finite gradients are outside the contract, and what their own blocks hold
+    afterwards is unspecified.  The step must still finish, and every other block
+    must match the oracle bit for bit, step after step."""
+    n = 6 * 2048 + 100
+    rng = np.random.default_rng(41)
+    p = host_params(n, pdt, rng)
+    hs = host_state(n)
+    dp, ds = to_dev(p, pdt), dev_state(n)
+    bad_blocks = (1, 4)
+    keep = np.ones(n, bool)
+    for b in bad_blocks:
+        keep[b * BLOCK:(b + 1) * BLOCK] = False
+    keep_blk = np.array([b not in bad_blocks for b in range(-(-n // BLOCK))])
+    say(f"non-finite gradients {pdt}/{gdt}")
+    for step in range(1, 4):
+        g = rng.normal(0, 1e-3, n).astype(np.float32)
+        g[1 * BLOCK + 7] = np.nan
+        g[1 * BLOCK + 300] = np.inf
+        g[4 * BLOCK + 2047] = -np.inf
+        g = oracle.f32_to_bf16_rne(g) if gdt == "bf16" else g
+        q.qopt_adam8bit_step([(dp, to_dev(g, gdt), *ds)], step=step, **HP)
+        with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+            out = oracle.adam8bit_step(p, g, *hs, step=step, param_dtype=pdt, grad_dtype=gdt, **HP)
+        p, hs = out[0], list(out[1:])
+        torch.cuda.synchronize()
+        got = [t.cpu().numpy() for t in ds]
+        what = f"(step {step}, {pdt}/{gdt})"
+        assert_state([got[0][keep], got[1][keep], got[2][keep_blk], got[3][keep_blk]],
+                     [hs[0][keep], hs[1][keep], hs[2][keep_blk], hs[3][keep_blk]], what)
+        assert_params(to_host(dp, pdt)[keep], p[keep], pdt, HP["lr"], what)
+        # the poisoned blocks' own parameters are NaN where their gradients were
+        gp = to_host(dp, pdt)
+        gp32 = oracle.bf16_to_f32(gp) if pdt == "bf16" else gp
+        assert np.isnan(gp32[1 * BLOCK + 7]) and np.isnan(gp32[4 * BLOCK + 2047])
+
+
 def test_late_step_and_zero_blocks(q):
     """A large step number, and blocks whose gradient and state are zero."""
     n = 4 * 2048
