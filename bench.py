@@ -241,6 +241,49 @@ def placements(torch, workloads, q, args):
                                                        for r in rounds]}}), flush=True)
 
 
+def ceiling(torch, workloads, q, args):
+    """The step against qopt_adam8bit_traffic_probe on the same buffers, timed in
+    turn: the probe moves exactly the step's bytes with its launch plan, grid and
+    access pattern but no arithmetic, so the ratio is how close the step comes to the
+    ceiling of its own access pattern on this placement of physical memory."""
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    tensors, sizes, pdt, gdt, label = make_workload(args.workload, torch, workloads, args.layout)
+    prepared = q.make_tensor_array(tensors)
+    step_bytes = algorithmic_bytes(sizes, 4 if pdt == torch.float32 else 2,
+                                   4 if gdt == torch.float32 else 2)
+    step = 0
+
+    def run_step():
+        nonlocal step
+        step += 1
+        q.qopt_adam8bit_step(tensors, step=step, _prepared=prepared, **hp)
+
+    def run_probe():
+        q.qopt_adam8bit_traffic_probe(tensors, _prepared=prepared)
+
+    for _ in range(5 + args.warmup):
+        run_step()
+    run_probe()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return step_bytes / (e0.elapsed_time(e1) / args.steps) / 1e6
+
+    rounds = [(timed(run_step), timed(run_probe)) for _ in range(3)]
+    print(json.dumps({"ceiling": {
+        "workload": label, "layout": args.layout, "steps_per_timing": args.steps,
+        "step_GB/s": [round(a, 1) for a, _ in rounds],
+        "probe_GB/s": [round(b, 1) for _, b in rounds],
+        "step_over_probe": [round(a / b, 4) for a, b in rounds],
+        "step_frac_of_8TB/s": [round(a / HBM_PEAK_GBS, 4) for a, _ in rounds]}}), flush=True)
+
+
 def bench_codec(torch, workloads, q, args):
     """Block-wise quantize and dequantize of 2^28 values 0.01 * Student-t(3)."""
     n = 1 << 28
@@ -435,6 +478,9 @@ def main():
     ap.add_argument("--placements", type=int, default=0, metavar="N",
                     help="only time the step on N copies of the workload held at once "
                          "(llama7b or gpt1p3b), each copy in turn")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only time the step against the traffic probe (same bytes and access "
+                         "pattern, no arithmetic) on the same buffers")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch copies of 4 GiB (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -456,6 +502,10 @@ def main():
         if args.workload not in ("llama7b", "gpt1p3b"):
             raise SystemExit("--placements takes the llama7b or gpt1p3b workload")
         return placements(torch, workloads, q, args)
+    if args.ceiling:
+        if args.workload not in ("llama7b", "llama7b_shard8", "gpt1p3b", "flat20b"):
+            raise SystemExit("--ceiling takes a step workload")
+        return ceiling(torch, workloads, q, args)
     if args.workload == "codec256m":
         return bench_codec(torch, workloads, q, args)
     if args.workload == "convert7b":

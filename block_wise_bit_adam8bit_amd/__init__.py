@@ -14,8 +14,8 @@ from ._lib import (  # noqa: F401
 from .functional import (  # noqa: F401
     SIGNED, UNSIGNED, nblocks, codebook, codebook_bytes, qopt_codebook_build,
     qopt_quantize_blockwise, qopt_dequantize_blockwise, qopt_adam8bit_step,
-    qopt_adam8bit_launch_count, qopt_quantize_blockwise_multi, qopt_dequantize_blockwise_multi,
-    make_tensor_array,
+    qopt_adam8bit_launch_count, qopt_adam8bit_traffic_probe, qopt_quantize_blockwise_multi,
+    qopt_dequantize_blockwise_multi, make_tensor_array,
 )
 from .checkpoint import (  # noqa: F401
     compress_moments, decompress_moments, compress_moments_multi, decompress_moments_multi,

@@ -99,6 +99,8 @@ _SIGNATURES = {
     "qopt_adam8bit_launch_count": (ctypes.c_int, [ctypes.POINTER(qopt_tensor), ctypes.c_int32,
                                                   ctypes.c_int, ctypes.c_int,
                                                   ctypes.POINTER(ctypes.c_int64)]),
+    "qopt_adam8bit_traffic_probe": (ctypes.c_int, [ctypes.POINTER(qopt_tensor), ctypes.c_int32,
+                                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
     "qopt_embedding_xavier_init": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                                   ctypes.c_int64, ctypes.c_uint64,
                                                   ctypes.c_void_p]),

@@ -867,6 +867,65 @@ adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qo
   }
 }
 
+// A measurement aid, not part of the method: the step's launch plan, grid, block
+// order, prefetch and every load and store of its vector path, with no arithmetic.
+// Each block's parameters, codes and block maxima are written back as read, and the
+// gradients are read and dropped, so the state is unchanged.  Timed against the step
+// on the same buffers it gives the ceiling of the step's access pattern.  Blocks
+// that are not on the vector path are skipped.
+template <typename PT, typename GT>
+__global__ void __launch_bounds__(kThreads) step_traffic_kernel(StepChunk c) {
+  typedef typename Vec4T<PT>::type PV;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const uint32_t stride = gridDim.x * kWaves;
+  const uint32_t total = c.block_start[c.npieces];
+  uint32_t blk = (blockIdx.x * kWaves + wave) * kStepRun;
+  if (blk >= total) return;
+  BlockRef cur = resolve(c, blk);
+  BlockIn<PT, GT> in;
+  if (cur.vec) load_block(in, cur, lane);
+  for (;;) {
+    uint32_t cm[kSlices], cv[kSlices];
+    float am = 0.0f, av = 0.0f;
+    if (cur.vec) {
+      PV* pout = reinterpret_cast<PV*>(static_cast<PT*>(cur.param) + cur.base);
+#pragma unroll
+      for (int s = 0; s < kSlices; ++s) {
+        asm volatile("" ::"v"(in.g[s]));  // the gradient is waited for, as the step does
+        st_wide(pout + s * kWave + lane, in.p[s]);
+        cm[s] = in.cm[s];
+        cv[s] = in.cv[s];
+      }
+      am = in.am;
+      av = in.av;
+    }
+    const uint32_t nblk = ((blk + 1) % kStepRun) ? blk + 1 : (blk / kStepRun + stride) * kStepRun;
+    const bool more = nblk < total;
+    BlockRef nxt = cur;
+    if (more) {
+      nxt = resolve(c, nblk);
+      if (nxt.vec) load_block(in, nxt, lane);
+    }
+    if (cur.vec) {
+      uint32_t* cmo = reinterpret_cast<uint32_t*>(cur.cm + cur.base);
+      uint32_t* cvo = reinterpret_cast<uint32_t*>(cur.cv + cur.base);
+#pragma unroll
+      for (int s = 0; s < kSlices; ++s) {
+        st_step_code(cmo + s * kWave + lane, cm[s]);
+        st_step_code(cvo + s * kWave + lane, cv[s]);
+      }
+      if (lane == 0) {
+        *cur.am = am;
+        *cur.av = av;
+      }
+    }
+    if (!more) break;
+    blk = nblk;
+    cur = nxt;
+  }
+}
+
 // ------------------------------------------------------------ host helpers
 
 struct DeviceInfo {
@@ -1259,6 +1318,45 @@ extern "C" int qopt_adam8bit_step(const qopt_tensor* tensors, int32_t ntensors, 
                                                cb_v_dev, s);
   return launch_step_chunks<uint16_t, uint16_t>(tensors, ntensors, psize, gsize, k, mode, cb_m_dev,
                                                   cb_v_dev, s);
+}
+
+// Workgroups per CU the step itself runs with (its occupancy), so that the traffic
+// probe moves the step's bytes with as many waves in flight.
+template <typename PT, typename GT>
+int step_wg_per_cu(int* per_cu) {
+  constexpr int kMode = std::is_same<PT, uint16_t>::value ? kScreen : kNoScreen;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, adam8bit_kernel<PT, GT, kMode>,
+                                                   kThreads, 0) != hipSuccess ||
+      *per_cu <= 0)
+    return QOPT_ELAUNCH;
+  return QOPT_OK;
+}
+
+template <typename PT, typename GT>
+int launch_traffic_probe(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size_t gsize,
+                         hipStream_t stream) {
+  int per_cu = 0;
+  const int rc = step_wg_per_cu<PT, GT>(&per_cu);
+  if (rc != QOPT_OK) return rc;
+  return launch_planned<StepChunk>(step_traffic_kernel<PT, GT>, per_cu, kStepRun, ntensors,
+                                   StepSize{tensors}, StepFill{tensors, psize, gsize}, stream);
+}
+
+extern "C" int qopt_adam8bit_traffic_probe(const qopt_tensor* tensors, int32_t ntensors,
+                                           int param_dtype, int grad_dtype, void* stream) {
+  bool any = false;
+  const int rc = check_step_tensors(tensors, ntensors, param_dtype, grad_dtype, &any);
+  if (rc != QOPT_OK || !any) return rc;
+  const size_t psize = param_dtype == QOPT_F32 ? 4 : 2;
+  const size_t gsize = grad_dtype == QOPT_F32 ? 4 : 2;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (param_dtype == QOPT_F32 && grad_dtype == QOPT_F32)
+    return launch_traffic_probe<float, float>(tensors, ntensors, psize, gsize, s);
+  if (param_dtype == QOPT_F32 && grad_dtype == QOPT_BF16)
+    return launch_traffic_probe<float, uint16_t>(tensors, ntensors, psize, gsize, s);
+  if (param_dtype == QOPT_BF16 && grad_dtype == QOPT_F32)
+    return launch_traffic_probe<uint16_t, float>(tensors, ntensors, psize, gsize, s);
+  return launch_traffic_probe<uint16_t, uint16_t>(tensors, ntensors, psize, gsize, s);
 }
 
 extern "C" int qopt_adam8bit_launch_count(const qopt_tensor* tensors, int32_t ntensors,

@@ -204,6 +204,19 @@ def qopt_adam8bit_launch_count(tensors, _prepared=None):
     return out.value
 
 
+def qopt_adam8bit_traffic_probe(tensors, _prepared=None):
+    """Measurement aid: the bytes of one qopt_adam8bit_step over these tensors, moved
+    with the step's launch plan and access pattern but no arithmetic (every buffer
+    keeps its contents), on torch's current stream."""
+    arr, pdt, gdt, dev = _prepared if _prepared is not None else make_tensor_array(tensors)
+    if dev is None:
+        return
+    with torch.cuda.device(dev):
+        rc = LIB.qopt_adam8bit_traffic_probe(arr, len(arr), pdt, gdt,
+                                             ctypes.c_void_p(_lib.stream_handle(dev)))
+    _lib.check("qopt_adam8bit_traffic_probe", rc)
+
+
 def qopt_adam8bit_step(tensors, *, lr, beta1, beta2, eps, step, _prepared=None):
     """One fused 8-bit Adam step over a list of (param, grad, m_codes, v_codes,
     m_absmax, v_absmax) tuples, updated in place on torch's current stream."""

@@ -229,6 +229,20 @@ int qopt_adam8bit_step(const qopt_tensor* tensors, int32_t ntensors, int param_d
 int qopt_adam8bit_launch_count(const qopt_tensor* tensors, int32_t ntensors, int param_dtype,
                                int grad_dtype, int64_t* launches);
 
+/*
+ * Measurement aid, not part of the method: moves exactly the bytes one
+ * qopt_adam8bit_step moves over these tensors, with the step's launch plan, grid
+ * (the step's own workgroups per CU), block order and prefetch, but no arithmetic:
+ * parameters, codes and block maxima are written back as read and gradients are read
+ * and dropped, so every buffer keeps its contents.  Timing it against the step on the
+ * same buffers gives the ceiling of the step's access pattern.  Only blocks on the
+ * step's vector path (full blocks of tensors whose pointers allow vector accesses)
+ * are moved.  Same argument checks as qopt_adam8bit_step (no codebooks or
+ * hyper-parameters); enqueued on `stream`.
+ */
+int qopt_adam8bit_traffic_probe(const qopt_tensor* tensors, int32_t ntensors, int param_dtype,
+                                int grad_dtype, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* qopt_status_string(int status);
 

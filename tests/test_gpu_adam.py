@@ -378,6 +378,32 @@ def test_non_finite_gradients_stay_in_their_blocks(q, pdt, gdt):
         assert np.isnan(gp32[1 * BLOCK + 7]) and np.isnan(gp32[4 * BLOCK + 2047])
 
 
+@pytest.mark.parametrize("pdt,gdt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "f32"),
+                                     ("bf16", "bf16")])
+def test_traffic_probe_keeps_every_buffer(q, pdt, gdt):
+    """The measurement aid moves the step's bytes and writes back what it read: after
+    it, parameters, gradients, codes and block maxima are bit for bit unchanged (tails
+    and misaligned views are skipped by it, full blocks rewritten)."""
+    sizes = [5 * 2048, 2048 + 3, 7, 3 * 2048]
+    rng = np.random.default_rng(51)
+    ts = []
+    for n in sizes:
+        nb = -(-n // BLOCK)
+        ts.append((to_dev(host_params(n, pdt, rng), pdt), to_dev(host_grads(n, gdt, rng), gdt),
+                   torch.from_numpy(rng.integers(0, 256, n).astype(np.uint8)).cuda(),
+                   torch.from_numpy(rng.integers(0, 256, n).astype(np.uint8)).cuda(),
+                   torch.from_numpy(rng.random(nb).astype(np.float32)).cuda(),
+                   torch.from_numpy(rng.random(nb).astype(np.float32)).cuda()))
+    before = [[t.clone() for t in tup] for tup in ts]
+    say(f"traffic probe {pdt}/{gdt}")
+    for _ in range(3):
+        q.qopt_adam8bit_traffic_probe(ts)
+    torch.cuda.synchronize()
+    for tup, ref in zip(ts, before):
+        for a, b in zip(tup, ref):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
 def test_late_step_and_zero_blocks(q):
     """A large step number, and blocks whose gradient and state are zero."""
     n = 4 * 2048
