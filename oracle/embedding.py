@@ -9,7 +9,7 @@ Sources:
   LayerNorm placed right after the embedding; "Stabilizations. BFloat 16": every
   LayerNorm is computed in tf32 / fp32 even when weights are bf16.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 * Xavier uniform is Glorot and Bengio's rule: U(-a, a) with a = sqrt(6 / (fan_in +
   fan_out)); for a [rows, dim] table the two fans are dim and rows.  a is computed
   in binary64 and rounded once to binary32; each weight is fl32(a * (2u - 1)).
