@@ -1,6 +1,7 @@
 """Adam8bit: a drop-in replacement for torch.optim.Adam whose two moments are stored
-as block-wise dynamic-tree 8-bit codes (the summary page's "two lines of code" swap:
-construct this optimizer instead of Adam).
+as block-wise dynamic-tree 8-bit codes.  As the summary page describes the switch, a
+training script constructs this optimizer where it constructed Adam and changes
+nothing else.
 
 State per parameter (allocated with torch on the parameter's device at its first
 step): ``m_codes`` / ``v_codes`` uint8 [n], ``m_absmax`` / ``v_absmax`` fp32
