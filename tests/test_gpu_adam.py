@@ -404,6 +404,44 @@ def test_traffic_probe_keeps_every_buffer(q, pdt, gdt):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
+@pytest.mark.parametrize("pdt,gdt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "f32"),
+                                     ("bf16", "bf16")])
+def test_random_hyperparameters(q, pdt, gdt):
+    """Thirty-two seeded hyper-parameter draws per dtype pair.  The draws cover:
+    - lr from 1e-5 to 1e-1;
+    - beta1 in [0, 0.99) and beta2 in [0.5, 0.9999);
+    - eps among 0, a subnormal, 1e-30, 1e-12, 1e-8 and 1e-6;
+    - steps 1 to 1000.
+
+    Every bf16 screen mode and fallback runs.  Each draw compares every element
+    after two consecutive steps."""
+    rng = np.random.default_rng(61 + sum(map(ord, pdt + gdt)))
+    for d in range(32):
+        hp = dict(lr=float(10.0 ** rng.uniform(-5, -1)), beta1=float(rng.uniform(0.0, 0.99)),
+                  beta2=float(1.0 - 10.0 ** rng.uniform(-4, np.log10(0.5))),
+                  eps=float(rng.choice([0.0, 1e-40, 1e-30, 1e-12, 1e-8, 1e-6])))
+        step0 = int(rng.choice([0, 1, 9, 999]))
+        sizes = [2 * 2048 + 77, 4096]
+        hp_p = [host_params(n, pdt, rng) for n in sizes]
+        hs = [host_state(n) for n in sizes]
+        dp = [to_dev(p, pdt) for p in hp_p]
+        ds = [dev_state(n) for n in sizes]
+        say(f"draw {d}: {hp} from step {step0 + 1} {pdt}/{gdt}")
+        for step in (step0 + 1, step0 + 2):
+            hg = [host_grads(n, gdt, rng, scale=float(10.0 ** rng.uniform(-6, 0))) for n in sizes]
+            q.qopt_adam8bit_step([(dp[i], to_dev(hg[i], gdt), *ds[i]) for i in range(len(sizes))],
+                                 step=step, **hp)
+            for i in range(len(sizes)):
+                out = oracle.adam8bit_step(hp_p[i], hg[i], *hs[i], step=step, param_dtype=pdt,
+                                           grad_dtype=gdt, **hp)
+                hp_p[i], hs[i] = out[0], list(out[1:])
+            torch.cuda.synchronize()
+            for i, n in enumerate(sizes):
+                what = f"(draw {d}, tensor {i}, step {step}, {hp}, {pdt}/{gdt})"
+                assert_state([t.cpu().numpy() for t in ds[i]], hs[i], what)
+                assert_params(to_host(dp[i], pdt), hp_p[i], pdt, hp["lr"], what)
+
+
 def test_late_step_and_zero_blocks(q):
     """A large step number, and blocks whose gradient and state are zero."""
     n = 4 * 2048
