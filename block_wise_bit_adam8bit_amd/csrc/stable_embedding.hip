@@ -195,8 +195,11 @@ fwd_vec_kernel(const WT* __restrict__ w, int64_t rows, int32_t dim, const int64_
   const int64_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kVecWaves;
   const float n_dim = static_cast<float>(dim);
-  for (int64_t t = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave; t < ntok; t += stride) {
-    const int64_t r = idx[t];
+  int64_t t0 = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave;
+  int64_t r_next = t0 < ntok ? idx[t0] : 0;
+  for (int64_t t = t0; t < ntok; t += stride) {
+    const int64_t r = r_next;
+    r_next = t + stride < ntok ? idx[t + stride] : 0;  // the next token's row, one step ahead
     OT* orow = out + t * dim;
     if (r < 0 || r >= rows) {
 #pragma unroll
