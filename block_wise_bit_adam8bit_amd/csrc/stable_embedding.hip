@@ -319,8 +319,8 @@ fwd_elem_kernel(const WT* __restrict__ w, int64_t rows, int64_t dim, const int64
 // order.  Every row is finished exactly once, by one wave, so dweight is updated
 // without atomics and every result is reproducible.
 
-constexpr int kSegChunk = 16;      // sorted tokens per chunk
-constexpr int kChunkWgPerCu = 8;   // resident chunk workgroups (two waves each) per CU
+constexpr int kSegChunk = 32;      // sorted tokens per chunk
+constexpr int kChunkWgPerCu = 4;   // chunk workgroups (two waves each) per CU, all resident
 
 // keys[t] = idx[t] for an index in [0, rows), else rows (sorts after every valid row).
 __global__ void __launch_bounds__(256) sort_keys_kernel(const int64_t* __restrict__ idx,
@@ -343,7 +343,7 @@ struct GroupAcc {
 
 // Finish row k from its summed upstream rows acc (mean / rstd of token t, one of the
 // row's tokens): dweight row += the LayerNorm backward of acc; add its dgamma / dbeta
-// terms to the wave's sums.
+// terms to the wave's sums.  The weight and gradient rows are loaded together.
 template <int S, typename WT>
 __device__ __forceinline__ void finish_row(const WT* __restrict__ w, int32_t dim, uint32_t k,
                                            int64_t t, const f32x4 (&acc)[S], const f32x4* gam,
@@ -354,12 +354,20 @@ __device__ __forceinline__ void finish_row(const WT* __restrict__ w, int32_t dim
   const WT* row = w + static_cast<int64_t>(k) * dim;
   const float mu = mean[t], rs = rstd[t];
   const float n_dim = static_cast<float>(dim);
+  float* drow = dweight + static_cast<int64_t>(k) * dim;
+  f32x4 xs[S], ds[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int c = s * 256 + 4 * lane < dim ? s * 256 + 4 * lane : 0;
+    xs[s] = Elem<WT>::load4(row, c);
+    ds[s] = *reinterpret_cast<const f32x4*>(drow + c);
+  }
   float c1 = 0.0f, c2 = 0.0f;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int c = s * 256 + 4 * lane;
     if (c < dim) {
-      const f32x4 x = Elem<WT>::load4(row, c);
+      const f32x4 x = xs[s];
       const f32x4 g = gam[s * kWave + lane];
       f32x4 xh, gg;
       xh.x = (x.x - mu) * rs;
@@ -387,14 +395,13 @@ __device__ __forceinline__ void finish_row(const WT* __restrict__ w, int32_t dim
   }
   const float m1 = wave_sum(c1) / n_dim;
   const float m2 = wave_sum(c2) / n_dim;
-  float* drow = dweight + static_cast<int64_t>(k) * dim;
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const int c = s * 256 + 4 * lane;
     if (c < dim) {
-      const f32x4 x = Elem<WT>::load4(row, c);
+      const f32x4 x = xs[s];
       const f32x4 g = gam[s * kWave + lane];
-      f32x4 d = *reinterpret_cast<const f32x4*>(drow + c);
+      f32x4 d = ds[s];
       d.x = d.x + (rs * (((acc[s].x * g.x) - m1) - (((x.x - mu) * rs) * m2)));
       d.y = d.y + (rs * (((acc[s].y * g.y) - m1) - (((x.y - mu) * rs) * m2)));
       d.z = d.z + (rs * (((acc[s].z * g.z) - m1) - (((x.z - mu) * rs) * m2)));
@@ -488,16 +495,14 @@ __device__ __forceinline__ int opaque_int(int x) {
 // (a slice past the row's end reads the row's first columns and adds zero) and the
 // loads are unconditional, so the compiler waits for exactly the row it adds; with
 // a branch per slice it waits for every outstanding load, the prefetched row
-// included.  Row-wide sums for a finished run are combined across the two waves
-// through LDS, in wave order.
+// included.  A run that ends in the chunk is finished at once: its weight row and its
+// gradient row are loaded together, and the row-wide sums are combined across the two
+// waves through LDS, in wave order.  Holding both rows takes up to 254 VGPRs, so 2
+// waves per SIMD; that beats loading the gradient row only after the sums at 3.
 // parts[chunk][0]: the sum over the chunk's tokens of a run that began in an earlier
 // chunk; parts[chunk][1]: of a run that begins in this chunk and goes on past it.
-// bf16 upstream rows leave room for 3 waves per SIMD (under 168 VGPRs with no
-// scratch); fp32 ones hold twice the registers per row in flight and keep 2.
-template <typename OT> constexpr int chunk_waves_per_simd() { return sizeof(OT) == 2 ? 3 : 2; }
-
 template <int S, typename WT, typename OT>
-__global__ void __launch_bounds__(kPairThreads, chunk_waves_per_simd<OT>())
+__global__ void __launch_bounds__(kPairThreads, 2)
 group_chunk_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
                    const uint32_t* __restrict__ keys, const int32_t* __restrict__ vals,
                    int64_t ntok, int64_t nchunks, const float* __restrict__ gamma,
@@ -584,12 +589,20 @@ group_chunk_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
           // finish row k: dweight[k] += LayerNorm backward of acc; gamma / beta terms
           const int c0 = opaque_int(col0);
           const WT* xrow = w + static_cast<int64_t>(k) * dim + c0;
+          float* drow = dweight + static_cast<int64_t>(k) * dim + c0;
           const float mu = mean[t], rs = rstd[t];
+          f32x4 xs[SH], ds[SH];
+#pragma unroll
+          for (int i = 0; i < SH; ++i) {
+            const int ci = c0 + 512 * i < dim ? 512 * i : 0;
+            xs[i] = Elem<WT>::load4(xrow, ci);
+            ds[i] = *reinterpret_cast<const f32x4*>(drow + ci);
+          }
           float c1 = 0.0f, c2 = 0.0f;
 #pragma unroll
           for (int i = 0; i < SH; ++i) {
             if (c0 + 512 * i < dim) {
-              const f32x4 x = Elem<WT>::load4(xrow, 512 * i);
+              const f32x4 x = xs[i];
               const f32x4 g = gam[(h + 2 * i) * kWave + lane];
               f32x4 xh, gg;
               xh.x = (x.x - mu) * rs;
@@ -625,13 +638,12 @@ group_chunk_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
           const float m1 = (red[0][0] + red[1][0]) / n_dim;
           const float m2 = (red[0][1] + red[1][1]) / n_dim;
           __syncthreads();
-          float* drow = dweight + static_cast<int64_t>(k) * dim + c0;
 #pragma unroll
           for (int i = 0; i < SH; ++i) {
             if (c0 + 512 * i < dim) {
-              const f32x4 x = Elem<WT>::load4(xrow, 512 * i);
+              const f32x4 x = xs[i];
               const f32x4 g = gam[(h + 2 * i) * kWave + lane];
-              f32x4 d = *reinterpret_cast<const f32x4*>(drow + 512 * i);
+              f32x4 d = ds[i];
               d.x = d.x + (rs * (((acc[i].x * g.x) - m1) - (((x.x - mu) * rs) * m2)));
               d.y = d.y + (rs * (((acc[i].y * g.y) - m1) - (((x.y - mu) * rs) * m2)));
               d.z = d.z + (rs * (((acc[i].z * g.z) - m1) - (((x.z - mu) * rs) * m2)));
@@ -694,14 +706,28 @@ group_span_sum_kernel(const uint32_t* __restrict__ keys, uint32_t rows, int32_t 
   const int s = static_cast<int>(task % S);
   uint32_t k = 0;
   if (ch >= nchunks || !span_starts(keys, rows, ntok, ch, &k)) return;
-  // the run ends at the first position past p1 whose key exceeds k (keys are sorted)
+  // the run ends at the first position past p1 whose key exceeds k (keys are sorted).
+  // It lies in [lo, hi], hi being the first position known to be past it; each round
+  // the 64 lanes probe 64 evenly spaced keys in [lo, hi) and keep the stretch where
+  // the keys pass k, so 2^16 tokens take three rounds of loads.
   int64_t lo = (ch + 1) * kSegChunk, hi = ntok;
   while (lo < hi) {
-    const int64_t mid = lo + (hi - lo) / 2;
-    if (keys[mid] <= k)
-      lo = mid + 1;
-    else
-      hi = mid;
+    const int64_t n = hi - lo;
+    const int64_t step = n <= kWave ? 1 : (n + kWave - 1) / kWave;
+    int64_t q = lo + (lane + 1) * step - 1;
+    q = q < hi - 1 ? q : hi - 1;
+    const uint64_t past = __ballot(keys[q] > k);
+    const int j = past ? __builtin_ctzll(past) : kWave;
+    if (n <= kWave) {
+      lo = hi = lo + (j < n ? j : n);
+    } else {
+      // probe j is the first past k, so the end is in (probe j - 1, probe j]
+      const int64_t qlo = lo + static_cast<int64_t>(j) * step;
+      const int64_t qj = lo + static_cast<int64_t>(j + 1) * step - 1;
+      const int64_t nhi = j == kWave ? hi : (qj < hi - 1 ? qj : hi - 1);
+      lo = qlo < hi ? qlo : hi;
+      hi = nhi;
+    }
   }
   const int64_t last = (lo - 1) / kSegChunk;  // the run's last chunk
   const int c = s * 256 + 4 * lane;
@@ -714,7 +740,8 @@ group_span_sum_kernel(const uint32_t* __restrict__ keys, uint32_t rows, int32_t 
   *reinterpret_cast<f32x4*>(tail) = acc;
 }
 
-// Step 2: one wave per chunk finishes the run that starts there, from its total.
+// Step 2: finish every run that crosses chunk boundaries from its total, one wave per
+// run, in a persistent grid whose workgroups keep one gradient slot each.
 template <int S, typename WT>
 __global__ void __launch_bounds__(kVecThreads)
 group_span_finish_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
@@ -735,9 +762,10 @@ group_span_finish_kernel(const WT* __restrict__ w, uint32_t rows, int32_t dim,
     ga.dg[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     ga.db[s] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  const int64_t ch = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave;
-  uint32_t k = 0;
-  if (ch < nchunks && span_starts(keys, rows, ntok, ch, &k)) {
+  for (int64_t ch = blockIdx.x * static_cast<int64_t>(kVecWaves) + wave; ch < nchunks;
+       ch += static_cast<int64_t>(gridDim.x) * kVecWaves) {
+    uint32_t k = 0;
+    if (!span_starts(keys, rows, ntok, ch, &k)) continue;
     const float* total = parts + (ch * 2 + 1) * dim;
     f32x4 acc[S];
 #pragma unroll
@@ -799,8 +827,9 @@ bwd_elem_kernel(const WT* __restrict__ w, int64_t rows, int64_t dim, const int64
 // dgamma[c] and dbeta[c] from the slots, in two deterministic steps.  Step 1:
 // workgroup (column block, group g) sums slots [g * per, (g + 1) * per): thread
 // (column c, subgroup j) adds the group's slots j, j + 4, ... in order, and the four
-// subgroup sums are added in subgroup order into level1[g].  Step 2 adds the groups'
-// sums in group order.
+// subgroup sums are added in subgroup order into level1[g].  Step 2 does the same over
+// the groups: subgroup j adds groups j, j + 4, ... (all its loads issued first), and
+// the four subgroup sums are added in subgroup order.
 constexpr int kReduceGroups = 64;
 
 __global__ void __launch_bounds__(256) bwd_reduce_step1_kernel(const float* __restrict__ ws,
@@ -834,15 +863,38 @@ __global__ void __launch_bounds__(256) bwd_reduce_step2_kernel(const float* __re
                                                                int64_t ngroups, int64_t dim,
                                                                float* __restrict__ dgamma,
                                                                float* __restrict__ dbeta) {
-  for (int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; c < dim;
-       c += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    float a = 0.0f, b = 0.0f;
-    for (int64_t g = 0; g < ngroups; ++g) {
-      a = a + level1[(2 * g) * dim + c];
-      b = b + level1[(2 * g + 1) * dim + c];
+  __shared__ float part[2][4][64];
+  const int col = threadIdx.x % 64;
+  const int sub = threadIdx.x / 64;
+  for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * 64; c0 < dim;
+       c0 += static_cast<int64_t>(gridDim.x) * 64) {
+    const int64_t c = c0 + col;
+    const int64_t cl = c < dim ? c : 0;
+    // all of the thread's loads are issued before the first add
+    constexpr int kPer = kReduceGroups / 4;
+    float va[kPer], vb[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t g = sub + 4 * i < ngroups ? sub + 4 * i : 0;
+      va[i] = ngroups > 0 ? level1[(2 * g) * dim + cl] : 0.0f;
+      vb[i] = ngroups > 0 ? level1[(2 * g + 1) * dim + cl] : 0.0f;
     }
-    dgamma[c] = a;
-    dbeta[c] = b;
+    float a = 0.0f, b = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (sub + 4 * i < ngroups) {
+        a = a + va[i];
+        b = b + vb[i];
+      }
+    }
+    part[0][sub][col] = a;
+    part[1][sub][col] = b;
+    __syncthreads();
+    if (sub == 0 && c < dim) {
+      dgamma[c] = ((part[0][0][col] + part[0][1][col]) + part[0][2][col]) + part[0][3][col];
+      dbeta[c] = ((part[1][0][col] + part[1][1][col]) + part[1][2][col]) + part[1][3][col];
+    }
+    __syncthreads();
   }
 }
 
@@ -944,14 +996,15 @@ struct GroupLayout {
   size_t parts = 0, slots = 0, total = 0;
   int64_t nchunks = 0;
   unsigned grid = 0;        // chunk kernel: two-wave workgroups, persistent
-  unsigned span_grid = 0;   // span finish kernel: one wave per chunk
+  unsigned span_grid = 0;   // span finish kernel: persistent, one wave per run
 };
 
 int group_layout(int64_t ntok, int64_t dim, int cus, GroupLayout* L) {
   L->nchunks = (ntok + kSegChunk - 1) / kSegChunk;
   const int64_t cap = static_cast<int64_t>(cus) * kChunkWgPerCu;
   L->grid = static_cast<unsigned>(L->nchunks < cap ? L->nchunks : cap);
-  L->span_grid = static_cast<unsigned>((L->nchunks + kVecWaves - 1) / kVecWaves);
+  const int64_t span_want = (L->nchunks + kVecWaves - 1) / kVecWaves;
+  L->span_grid = static_cast<unsigned>(span_want < cus ? span_want : cus);
   size_t sb = 0;
   if (rocprim::radix_sort_pairs(nullptr, sb, static_cast<const uint32_t*>(nullptr),
                                 static_cast<uint32_t*>(nullptr), static_cast<const int32_t*>(nullptr),
@@ -1175,7 +1228,7 @@ extern "C" int qopt_stable_embedding_backward(const void* weight_dev, int weight
   int rc = device_cus(&cus);
   if (rc != QOPT_OK) return rc;
   const unsigned rgrid = static_cast<unsigned>(
-      (dim + 255) / 256 < static_cast<int64_t>(cus) * 4 ? (dim + 255) / 256 : static_cast<int64_t>(cus) * 4);
+      (dim + 63) / 64 < static_cast<int64_t>(cus) * 16 ? (dim + 63) / 64 : static_cast<int64_t>(cus) * 16);
   if (ntokens == 0) {
     hipLaunchKernelGGL(bwd_reduce_step2_kernel, dim3(rgrid), dim3(256), 0, s, nullptr, int64_t{0},
                        dim, dgamma_dev, dbeta_dev);
