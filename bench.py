@@ -432,11 +432,13 @@ def bench_embed(torch, workloads, q, args):
     tf = timed(fwd)
     tb = timed(bwd)
     uniq = int(len(set(ids_host.tolist())))
-    slots = ws.numel() // (2 * dim * 4)
-    # minimal HBM traffic: each distinct row once, token-major arrays once
+    # minimal HBM traffic of the operation: each distinct row once, token-major arrays
+    # once (ids 8 B, mean and rstd 4 B each); the backward also reads and writes each
+    # distinct row's gradient once.  The workspace (sort keys, per-chunk partial sums,
+    # dgamma / dbeta slots) is the implementation's own overhead and is not counted.
     fwd_bytes = uniq * dim * 4 + ntok * dim * 2 + ntok * 16 + 2 * dim * 4
     bwd_bytes = (uniq * dim * 4 + ntok * dim * 2 + ntok * 16 + uniq * dim * 8
-                 + slots * 2 * dim * 4 * 2 + 3 * dim * 4)
+                 + 3 * dim * 4)
     # bytes the kernels request (every token's row read, every token's gradient row
     # added), served partly by the caches when ids repeat
     fwd_req = ntok * dim * (4 + 2) + ntok * 16
@@ -455,7 +457,7 @@ def bench_embed(torch, workloads, q, args):
                 "config": {"workload": f"embed7b: Xavier-initialised {rows} x {dim} fp32 table, "
                                        f"{ntok} Zipf(1) token ids ({uniq} distinct), LayerNorm "
                                        "to bf16, bf16 upstream gradient N(0,1)",
-                           "distinct_rows": uniq, "gradient_slots": slots},
+                           "distinct_rows": uniq, "workspace_bytes": ws.numel()},
                 "kernels": {"forward": k(tf, fwd_bytes, fwd_req),
                             "backward": k(tb, bwd_bytes, bwd_req)}}
     print(json.dumps(out_line), flush=True)

@@ -320,7 +320,9 @@ fwd_elem_kernel(const WT* __restrict__ w, int64_t rows, int64_t dim, const int64
 // without atomics and every result is reproducible.
 
 constexpr int kSegChunk = 32;      // sorted tokens per chunk
-constexpr int kChunkWgPerCu = 4;   // chunk workgroups (two waves each) per CU, all resident
+// chunk workgroups (two waves each) per CU: twice what fits at once, so that workgroups
+// whose chunks finish many runs do not hold up the rest
+constexpr int kChunkWgPerCu = 8;
 
 // keys[t] = idx[t] for an index in [0, rows), else rows (sorts after every valid row).
 __global__ void __launch_bounds__(256) sort_keys_kernel(const int64_t* __restrict__ idx,
