@@ -192,6 +192,44 @@ def test_forward_and_backward(q, rows, dim, wdt, odt):
         assert torch.equal(dw_a, dw_b)
 
 
+@pytest.mark.parametrize("dim", [256, 4096])
+@pytest.mark.parametrize("lengths", [
+    [1, 31, 32, 33, 63, 64, 65, 96, 200, 1, 2, 31],   # runs ending on and beside 32-token marks
+    [517],                                              # one row takes every token
+    [300, 217],                                         # two long runs, the last ending at the end
+    [1] * 40 + [140] + [1] * 30,                        # a long run among single tokens
+])
+def test_run_layouts_across_chunks(q, dim, lengths):
+    """Sorted runs of chosen lengths, so that runs start and end on, just before and just
+    after chunk boundaries of any power-of-two chunk size up to 64, span many chunks,
+    or cover the whole batch: every table-gradient row, dgamma and dbeta against the
+    oracle."""
+    ntok = sum(lengths)
+    say(f"run layouts dim {dim} lengths {lengths[:6]}... ({len(lengths)} runs, {ntok} tokens)")
+    rows = len(lengths) + 3
+    rng = np.random.default_rng(dim + ntok)
+    w = rng.uniform(-0.05, 0.05, (rows, dim)).astype(np.float32)
+    gamma = rng.normal(1.0, 0.25, dim).astype(np.float32)
+    beta = rng.normal(0.0, 0.1, dim).astype(np.float32)
+    # run r (in sorted order) is row r + 1; tokens in random order
+    idx = rng.permutation(np.repeat(np.arange(1, len(lengths) + 1), lengths)).astype(np.int64)
+    dy = (f32_to_bf16_rne(rng.normal(0.0, 1.0, (ntok, dim)).astype(np.float32))
+          .astype(np.uint32) << np.uint32(16)).view(np.float32)
+    tw, tidx = to_dev(w, "f32"), torch.from_numpy(idx).cuda()
+    tg, tb = to_dev(gamma, "f32"), to_dev(beta, "f32")
+    out, mean, rstd = q.qopt_stable_embedding_forward(tw, tidx, tg, tb, 1e-5, torch.bfloat16)
+    dw, dg, db = q.qopt_stable_embedding_backward(tw, tidx, tg, mean, rstd, to_dev(dy, "bf16"))
+    x = w.astype(np.float64)[idx]
+    rdw, rdg, rdb, tdw, tdg, tdb = backward_ref_and_tol(x, idx, rows, gamma.astype(np.float64),
+                                                        beta.astype(np.float64),
+                                                        dy.astype(np.float64), 1e-5)
+    torch.cuda.synchronize()
+    assert_within(host(dw), rdw, tdw, "dweight")
+    assert not host(dw)[0].any() and not host(dw)[-2:].any()   # rows no token uses
+    assert_within(host(dg), rdg, tdg, "dgamma")
+    assert_within(host(db), rdb, tdb, "dbeta")
+
+
 def test_misaligned_views_take_the_element_path(q):
     rows, dim, ntok = 64, 256, 100
     w, idx, gamma, beta, dy = _inputs(rows, dim, ntok, seed=9)
