@@ -440,26 +440,6 @@ __device__ __forceinline__ void write_slot(const GroupAcc<S>& ga, f32x4* comb_g,
   }
 }
 
-template <int S, typename OT>
-__device__ __forceinline__ void add_row(f32x4 (&acc)[S], const OT* __restrict__ row, int32_t dim,
-                                        int lane) {
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int c = s * 256 + 4 * lane;
-    if (c < dim) acc[s] = acc[s] + Elem<OT>::load4(row, c);
-  }
-}
-
-template <int S>
-__device__ __forceinline__ void store_row(float* __restrict__ dst, const f32x4 (&acc)[S],
-                                          int32_t dim, int lane) {
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int c = s * 256 + 4 * lane;
-    if (c < dim) *reinterpret_cast<f32x4*>(dst + c) = acc[s];
-  }
-}
-
 // Raw 4-element groups of an upstream-gradient row as loaded (fp32 or packed bf16).
 template <typename OT> struct Raw4;
 template <> struct Raw4<float> {
