@@ -44,6 +44,18 @@ def algorithmic_bytes(sizes, pbytes, gbytes):
     return total
 
 
+def embedding_bytes(distinct, ntok, dim):
+    """Minimal HBM bytes of one Stable Embedding forward and backward (fp32 table, bf16
+    outputs and upstream gradients): each distinct row once, token-major arrays once
+    (ids 8 B, mean and rstd 4 B each per token); the backward also reads and writes each
+    distinct row's fp32 gradient once.  The backward's workspace (sort keys, per-chunk
+    partial sums, dgamma / dbeta slots) is the implementation's own overhead and is not
+    counted.  Returns (forward, backward)."""
+    fwd = distinct * dim * 4 + ntok * dim * 2 + ntok * 16 + 2 * dim * 4
+    bwd = distinct * dim * 4 + ntok * dim * 2 + ntok * 16 + distinct * dim * 8 + 3 * dim * 4
+    return fwd, bwd
+
+
 def kernel_code_hash(text=None):
     """sha256 of the step kernel's source with comments removed and whitespace
     collapsed: it changes with the code, not with its comments."""
@@ -432,13 +444,7 @@ def bench_embed(torch, workloads, q, args):
     tf = timed(fwd)
     tb = timed(bwd)
     uniq = int(len(set(ids_host.tolist())))
-    # minimal HBM traffic of the operation: each distinct row once, token-major arrays
-    # once (ids 8 B, mean and rstd 4 B each); the backward also reads and writes each
-    # distinct row's gradient once.  The workspace (sort keys, per-chunk partial sums,
-    # dgamma / dbeta slots) is the implementation's own overhead and is not counted.
-    fwd_bytes = uniq * dim * 4 + ntok * dim * 2 + ntok * 16 + 2 * dim * 4
-    bwd_bytes = (uniq * dim * 4 + ntok * dim * 2 + ntok * 16 + uniq * dim * 8
-                 + 3 * dim * 4)
+    fwd_bytes, bwd_bytes = embedding_bytes(uniq, ntok, dim)
     # bytes the kernels request (every token's row read, every token's gradient row
     # added), served partly by the caches when ids repeat
     fwd_req = ntok * dim * (4 + 2) + ntok * 16

@@ -2,7 +2,7 @@
 
 CPU tests cover:
 - the refusal of more than one GPU;
-- the algorithmic-bytes formula;
+- the algorithmic-bytes formulas of the step and the embedding layer;
 - the guards on the committed traffic file;
 - the CPU-baseline record.
 
@@ -36,6 +36,17 @@ def test_algorithmic_bytes():
     assert bench.algorithmic_bytes([1, 2048], 2, 2) == 1 * 10 + 16 + 2048 * 10 + 16
     assert bench.algorithmic_bytes([2048], 4, 4) == 2048 * 16 + 16
     assert bench.algorithmic_bytes([], 4, 2) == 0
+
+
+def test_embedding_bytes():
+    # forward: 3 distinct fp32 rows of 8, 5 bf16 output rows, 16 B per token, gamma and beta
+    fwd, bwd = bench.embedding_bytes(3, 5, 8)
+    assert fwd == 3 * 32 + 5 * 16 + 5 * 16 + 2 * 32
+    # backward: the same reads, each distinct row's fp32 gradient read and written, gamma
+    # read, dgamma and dbeta written; nothing for the workspace
+    assert bwd == 3 * 32 + 5 * 16 + 5 * 16 + 3 * 64 + 3 * 32
+    # the embedding workload's figures: 12,999 distinct rows of 4096, 65,536 tokens
+    assert bench.embedding_bytes(12999, 65536, 4096)[1] == 1_176_895_488
 
 
 def test_kernel_code_hash_ignores_comments_only():
