@@ -117,13 +117,15 @@ __device__ __forceinline__ void stage_codebook(qopt_codebook* dst, const qopt_co
   for (int i = threadIdx.x; i < kRows; i += kThreads) d[i] = s[i];
 }
 
-// Maximum over the wave of a non-negative float (a magnitude or a second moment),
-// returned to every lane.  For non-negative binary32 values the order of the bit
-// patterns as unsigned integers is the order of the values, so the reduction runs on
-// the bits with integer max: four DPP steps inside each row of 16 lanes (swap
-// neighbours, swap pairs, mirror the half rows, mirror the rows), two row broadcasts
-// that carry the row maxima up to lane 63, then one read of lane 63 into a scalar
-// register.  No LDS traffic and no waits on it, unlike a shuffle-based butterfly.
+// Maximum over the wave of the bit patterns of non-negative floats (magnitudes or
+// second moments), as a float, returned to every lane.  For non-negative binary32
+// values the order of the bit patterns as unsigned integers is the order of the
+// values, and every NaN pattern lies above +inf, so a NaN anywhere in the block makes
+// its maximum a NaN, as a maximum over the values that propagates NaN would.  Four
+// DPP steps inside each row of 16 lanes (swap neighbours, swap pairs, mirror the half
+// rows, mirror the rows), two row broadcasts that carry the row maxima up to lane 63,
+// then one read of lane 63 into a scalar register.  No LDS traffic and no waits on it,
+// unlike a shuffle-based butterfly.
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 template <int kCtrl, int kRowMask>
 __device__ __forceinline__ uint32_t dpp_max(uint32_t u) {
@@ -131,8 +133,7 @@ __device__ __forceinline__ uint32_t dpp_max(uint32_t u) {
   return umax(u, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
                      0, static_cast<int>(u), kCtrl, kRowMask, 0xF, false)));
 }
-__device__ __forceinline__ float wave_max(float x) {
-  uint32_t u = __float_as_uint(x);
+__device__ __forceinline__ float wave_max_bits(uint32_t u) {
   u = dpp_max<0xB1, 0xF>(u);   // quad_perm [1,0,3,2]
   u = dpp_max<0x4E, 0xF>(u);   // quad_perm [2,3,0,1]
   u = dpp_max<0x141, 0xF>(u);  // row_half_mirror
@@ -140,6 +141,12 @@ __device__ __forceinline__ float wave_max(float x) {
   u = dpp_max<0x142, 0xA>(u);  // row_bcast:15 into rows 1 and 3
   u = dpp_max<0x143, 0xC>(u);  // row_bcast:31 into rows 2 and 3
   return __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), 63)));
+}
+
+// Maximum that propagates NaN (v_maximum3_f32 on gfx950, which also folds absolute
+// values and a third operand): a block with a NaN in it has a NaN maximum.
+__device__ __forceinline__ float max_nan(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -174,26 +181,34 @@ __device__ __forceinline__ Encoder make_encoder(const qopt_codebook* lds_cb) {
 // bucket 0 and is clamped to the last bucket above it, so every index stays inside
 // the tables for any input and any table contents (bucket bytes <= 255, thresh has
 // >= 257 entries).
-__device__ __forceinline__ uint32_t encode_mag(const Encoder& e, float a) {
+__device__ __forceinline__ uint32_t encode_mag(const Encoder& e, uint32_t last_bucket, float a) {
   uint32_t i = __builtin_elementwise_sub_sat(__float_as_uint(a) >> 15, e.key0);
-  i = i < e.last_bucket ? i : e.last_bucket;
+  i = i < last_bucket ? i : last_bucket;
   const uint32_t b = e.cb->bucket[i];
   return b + (a >= e.cb->thresh[b + 1] ? 1u : 0u);
 }
 
-// Per-block normalisation: reciprocal, stored absmax and effective sign mask.
+// Per-block normalisation: reciprocal, stored absmax, effective sign mask and the
+// highest bucket the encoder may use (all wave-uniform, held in scalar registers).
 struct BlockScale {
   float r;
   float absmax;
   uint32_t sign_mask;
+  uint32_t last_bucket;
 };
 
-__device__ __forceinline__ BlockScale block_scale(float amax, uint32_t sign_mask) {
+// Zero and subnormal blocks, and blocks whose maximum is NaN, store absmax 0 and
+// every code 0: their reciprocal is 0, so every finite element normalises to 0, and
+// the encoder is held to bucket 0, where 0 and any NaN (an infinite or NaN element
+// times 0) both encode as 0.
+__device__ __forceinline__ BlockScale block_scale(float amax, uint32_t sign_mask,
+                                                  const Encoder& e) {
   BlockScale s;
-  const bool ok = amax >= FLT_MIN;  // zero or subnormal blocks store absmax 0, codes 0
+  const bool ok = amax >= FLT_MIN;
   s.r = ok ? 1.0f / amax : 0.0f;
   s.absmax = ok ? amax : 0.0f;
   s.sign_mask = ok ? sign_mask : 0u;
+  s.last_bucket = ok ? e.last_bucket : 0u;
   return s;
 }
 
@@ -204,7 +219,7 @@ __device__ __forceinline__ BlockScale block_scale(float amax, uint32_t sign_mask
 __device__ __forceinline__ uint32_t encode_signed(const Encoder& e, const BlockScale& s, float x) {
   const float a = fabsf(x) * s.r;
   uint32_t i = __builtin_elementwise_sub_sat(__float_as_uint(a) >> 15, e.key0);
-  i = i < e.last_bucket ? i : e.last_bucket;
+  i = i < s.last_bucket ? i : s.last_bucket;
   const uint32_t b = e.cb->bucket[i];
   const uint32_t sign = x < 0.0f ? s.sign_mask : 0u;
   return (b + sign) + (a >= e.cb->thresh[b + 1] ? 1u : 0u);
@@ -212,7 +227,7 @@ __device__ __forceinline__ uint32_t encode_signed(const Encoder& e, const BlockS
 
 // Second moments are sums of non-negative terms, so no sign bit is ever set.
 __device__ __forceinline__ uint32_t encode_nonneg(const Encoder& e, const BlockScale& s, float x) {
-  return encode_mag(e, x * s.r);
+  return encode_mag(e, s.last_bucket, x * s.r);
 }
 
 // ---------------------------------------------------------- codec kernels
@@ -339,8 +354,8 @@ quantize_kernel(CodecChunk c, const qopt_codebook* cb_g) {
 #pragma unroll
     for (int s = 0; s < kSlices; ++s)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) amax = fmaxf(amax, fabsf(x[s][j]));
-    const BlockScale sc = block_scale(wave_max(amax), sign_mask);
+      for (int j = 0; j < 4; ++j) amax = max_nan(amax, fabsf(x[s][j]));
+    const BlockScale sc = block_scale(wave_max_bits(__float_as_uint(amax)), sign_mask, enc);
 
     const uint32_t nblk = blk + stride;
     const bool more = nblk < total;
@@ -435,6 +450,14 @@ struct AdamScalars {
 // not at all, or screened, or screened with slices holding a subnormal second
 // moment sent to the correctly rounded sequence as well.
 enum ScreenMode : int { kNoScreen = 0, kScreen = 1, kScreenSubCheck = 2 };
+
+// Register budget per instantiation: the bf16 kernels of the two rare modes (the
+// screen off, or with its subnormal test) need a few more registers than three waves
+// per SIMD allow, and run at two waves per SIMD rather than spill.
+template <typename PT, int kMode> constexpr int step_waves() {
+  return (std::is_same<PT, uint16_t>::value && kMode != kScreen) ? 2
+                                                                  : StepShape<PT>::kWavesPerSimd;
+}
 
 // One launch's work: up to kMaxTensors pieces, each a run of whole blocks of one
 // tensor.  Large tensors may be split over several launches so that every launch
@@ -607,8 +630,6 @@ __device__ __forceinline__ void load_block(BlockIn<PT, GT>& in, const BlockRef& 
   const GV* g = reinterpret_cast<const GV*>(static_cast<const GT*>(r.grad) + r.base) + l;
   const uint32_t* cm = reinterpret_cast<const uint32_t*>(r.cm + r.base) + l;
   const uint32_t* cv = reinterpret_cast<const uint32_t*>(r.cv + r.base) + l;
-  in.am = *r.am;
-  in.av = *r.av;
 #pragma unroll
   for (int s = 0; s < kSlices; ++s) {
     in.p[s] = ld_wide(p + s * kWave);
@@ -616,6 +637,9 @@ __device__ __forceinline__ void load_block(BlockIn<PT, GT>& in, const BlockRef& 
     in.cm[s] = ld_step_code(cm + s * kWave);
     in.cv[s] = ld_step_code(cv + s * kWave);
   }
+  // the block maxima after the streams: loaded first they measured 0.8 % slower
+  in.am = *r.am;
+  in.av = *r.av;
 }
 
 // A wave's second-moment stash in LDS: slice s of lane l at 16 bytes per lane, so
@@ -724,8 +748,8 @@ __device__ __forceinline__ void update_vec(const AdamScalars& k, const qopt_code
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      mmax = fmaxf(mmax, fabsf(m[s][j]));
-      vmax = fmaxf(vmax, v[s][j]);
+      mmax = max_nan(mmax, fabsf(m[s][j]));
+      vmax = max_nan(vmax, v[s][j]);
     }
     if constexpr (StepShape<PT>::kVInLds) stash_v(vstash, s, lane, v[s]);
     PV pv;
@@ -761,8 +785,8 @@ __device__ __forceinline__ void update_scalar(const AdamScalars& k, const qopt_c
         const float p = adam_element(k, load1<PT>(pb, e), load1<GT>(gb, e), m_prev, v_prev,
                                      m[s][j], v[s][j]);
         store1<PT>(pb, e, p);
-        mmax = fmaxf(mmax, fabsf(m[s][j]));
-        vmax = fmaxf(vmax, v[s][j]);
+        mmax = max_nan(mmax, fabsf(m[s][j]));
+        vmax = max_nan(vmax, v[s][j]);
       }
     }
   if constexpr (StepShape<PT>::kVInLds) {
@@ -777,8 +801,8 @@ __device__ __forceinline__ void requantize(const Encoder& em, const Encoder& ev,
                                            uint32_t sign_v, const BlockRef& r, int lane,
                                            const float m[kSlices][4], const float v[kSlices][4],
                                            const float* vstash, float mmax, float vmax) {
-  const BlockScale sm = block_scale(wave_max(mmax), sign_m);
-  const BlockScale sv = block_scale(wave_max(vmax), sign_v);
+  const BlockScale sm = block_scale(wave_max_bits(__float_as_uint(mmax)), sign_m, em);
+  const BlockScale sv = block_scale(wave_max_bits(__float_as_uint(vmax)), sign_v, ev);
   uint32_t* cmo = reinterpret_cast<uint32_t*>(r.cm + r.base);
   uint32_t* cvo = reinterpret_cast<uint32_t*>(r.cv + r.base);
 #pragma unroll
@@ -819,7 +843,7 @@ __device__ __forceinline__ void requantize(const Encoder& em, const Encoder& ev,
 // registers the update no longer needs), so memory stays busy through the
 // requantization phase.
 template <typename PT, typename GT, int kMode>
-__global__ void __launch_bounds__(kThreads, StepShape<PT>::kWavesPerSimd)
+__global__ void __launch_bounds__(kThreads, (step_waves<PT, kMode>()))
 adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qopt_codebook* cbv_g) {
   constexpr bool kVInLds = StepShape<PT>::kVInLds;
   __shared__ __align__(16) qopt_codebook cb[2];

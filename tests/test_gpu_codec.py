@@ -114,6 +114,43 @@ def test_codec_special_blocks(q, kind):
 
 
 @pytest.mark.parametrize("kind", KINDS)
+def test_codec_non_finite_blocks(q, kind):
+    """Blocks holding NaN or infinite values (outside the method's contract) still
+    match the oracle code for code: a NaN anywhere makes the block's maximum NaN, so
+    it is stored as absmax 0 with every code 0; an infinite maximum gives a reciprocal
+    of 0, so finite elements encode as 0 (with their sign) and infinite ones as the
+    top code.  Neighbouring blocks are untouched (block independence)."""
+    B = 2048
+    rng = np.random.default_rng(21)
+    base = workloads.student_t3_host(9 * B + 100, seed=21)
+    x = base.copy()
+    x[1 * B + 5] = np.nan                       # one NaN
+    x[2 * B + 9] = np.inf                       # one +inf
+    x[3 * B + 2047] = -np.inf                   # one -inf, last lane of the last slice
+    x[4 * B: 5 * B] = np.nan                    # all NaN
+    x[5 * B + 3] = np.inf                       # NaN and inf together
+    x[5 * B + 4] = np.nan
+    x[6 * B: 7 * B] = -np.inf                   # all -inf
+    x[7 * B + rng.integers(0, B, 40)] = np.inf  # many +inf
+    x[9 * B + 50] = np.nan                      # in the short tail block
+    if kind == oracle.UNSIGNED:
+        x = np.abs(x)
+    say(f"codec non-finite blocks kind={kind}")
+    with np.errstate(invalid="ignore"):
+        c_ref, a_ref = oracle.quantize_blockwise(x, kind)
+    c, a = q.qopt_quantize_blockwise(torch.from_numpy(x).cuda(), kind)
+    torch.cuda.synchronize()
+    got_c, got_a = c.cpu().numpy(), a.cpu().numpy()
+    bad = np.nonzero(got_c != c_ref)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, first at {bad[:5]}"
+    assert np.array_equal(got_a.view(np.uint32), a_ref.view(np.uint32))
+    # the oracle's reading, restated: NaN blocks zero, infinite blocks keep inf
+    assert a_ref[1] == 0 and a_ref[4] == 0 and a_ref[5] == 0 and a_ref[9] == 0
+    assert not c_ref[4 * B: 6 * B].any()
+    assert np.isinf(a_ref[2]) and np.isinf(a_ref[7]) and np.isfinite(a_ref[8])
+
+
+@pytest.mark.parametrize("kind", KINDS)
 def test_exhaustive_unit_interval(q, kind):
     """Every binary32 in [0, 1] (and, signed, its negation) is quantized in blocks
     whose absmax is exactly 1.0, so the kernel encodes the value itself.  The codes

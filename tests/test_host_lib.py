@@ -118,6 +118,23 @@ def test_bucket_tables_reproduce_nearest_rule(kind):
     assert got.max() == nmag - 1
 
 
+@pytest.mark.parametrize("kind", [oracle.SIGNED, oracle.UNSIGNED])
+def test_bucket_table_ends_give_the_oracle_codes_of_non_finite_values(kind):
+    """The two ends of the encoder's tables that non-finite values reach.  A block with
+    an infinite element has a reciprocal of 0, so that element normalises to NaN (inf
+    times 0); the encoder clamps its key into the last bucket and the threshold test is
+    false for NaN, so it takes the last bucket's first index, which must be the top
+    magnitude index, the index the oracle's nearest rule gives a NaN.  A block that is
+    stored as zero (maximum NaN, zero or subnormal) is held to bucket 0, whose first
+    index must be 0 and whose next threshold must lie above 0."""
+    cb, dec, th, bk = _tables(kind)
+    mags = oracle.magnitudes_f32(kind)
+    assert int(bk[cb.nbuckets - 1]) == cb.nmag - 1
+    assert int(oracle.nearest_magnitude_index(mags, np.float32(np.nan))) == cb.nmag - 1
+    assert np.isinf(th[cb.nmag]) and th[cb.nmag] > 0   # nothing passes the top code
+    assert int(bk[0]) == 0 and th[1] > 0
+
+
 def test_argument_checks_return_before_any_launch():
     L = qopt.LIB
     null = ctypes.c_void_p(0)
