@@ -8,6 +8,10 @@ trajectories the oracle can run on their own because blocks are independent.
 """
 
 import copy
+import json
+import os
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -47,7 +51,7 @@ def to_dev(a, dtype):
 def to_host(t, dtype):
     if dtype == "bf16":
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
-    return t.cpu().numpy()
+    return t.cpu().numpy()  # fp32 values or uint8 codes
 
 
 def host_state(n):
@@ -570,64 +574,88 @@ def test_optimizer_per_parameter_steps(q):
 # ------------------------------------------------------- full-size, sampled
 
 
-def sampled_trajectory(q, shapes, pdt, gdt, steps, seed, grad_fill, sample_count,
+ORACLE_WORKERS = 8   # child processes running the oracle (numpy only)
+
+
+def run_oracle_blocks(inputs, cfg, nblocks, tmpdir):
+    """The oracle's trajectory of the gathered full blocks (``inputs``: p0 and the
+    gradients of every step, blocks one after another), split over ORACLE_WORKERS
+    child processes by block; returns the final parameters, codes and block maxima."""
+    worker = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_blocks_worker.py")
+    cuts = np.linspace(0, nblocks, ORACLE_WORKERS + 1).astype(np.int64)
+    procs = []
+    for w in range(ORACLE_WORKERS):
+        a, b = int(cuts[w]) * BLOCK, int(cuts[w + 1]) * BLOCK
+        if a == b:
+            continue
+        fin, fout = os.path.join(tmpdir, f"in{w}.npz"), os.path.join(tmpdir, f"out{w}.npz")
+        np.savez(fin, cfg=np.array(json.dumps(cfg)), **{k: v[a:b] for k, v in inputs.items()})
+        procs.append((fout, subprocess.Popen([sys.executable, worker, fin, fout])))
+    outs = []
+    for fout, pr in procs:
+        assert pr.wait() == 0, "oracle worker failed"
+        outs.append(np.load(fout))
+    return {k: np.concatenate([o[k] for o in outs]) for k in ("p", "cm", "cv", "am", "av")}
+
+
+def sampled_trajectory(q, shapes, pdt, gdt, steps, seed, grad_fill, tmp_path, sample_frac=0.01,
                        extra_blocks=()):
-    """Run ``steps`` GPU steps over a full parameter set from zero state and follow
-    the sampled blocks' trajectories in the oracle (blocks are independent)."""
+    """Run ``steps`` GPU steps over a full parameter set from zero state and follow at
+    least ``sample_frac`` of its blocks in the oracle, which can step them on their
+    own because blocks are independent: every tensor's first and last block, the
+    blocks on either side of every launch split of the step's plan (launches cover
+    equal runs of the flattened blocks), the extra blocks, and distinct blocks drawn
+    uniformly.  The parameter set lies in flat buffers with every tensor starting on
+    a block boundary and every block full, so a sampled block is one row of the
+    buffers viewed as [blocks, 2048]."""
     dt_p, dt_g = DT[pdt], DT[gdt]
     offs = np.cumsum([0] + [n for _, n in shapes])
+    assert all(n % BLOCK == 0 for _, n in shapes)
     total = int(offs[-1])
+    nblk = total // BLOCK
     say(f"allocating {len(shapes)} tensors, {total} params ({pdt} params, {gdt} grads)")
     P = torch.empty(total, dtype=dt_p, device="cuda")
     G = torch.empty(total, dtype=dt_g, device="cuda")
+    CM = torch.zeros(total, dtype=torch.uint8, device="cuda")
+    CV = torch.zeros_like(CM)
+    AM = torch.zeros(nblk, dtype=torch.float32, device="cuda")
+    AV = torch.zeros_like(AM)
     workloads.fill_normal_(P, 0.02, seed)
     tensors = []
     for ti, (name, n) in enumerate(shapes):
-        o = int(offs[ti])
-        tensors.append((P[o:o + n], G[o:o + n], *dev_state(n)))
-    nblk_per = [-(-n // BLOCK) for _, n in shapes]
-    bstart = np.cumsum([0] + nblk_per)
-    must = list(extra_blocks) + [int(bstart[i]) for i in range(len(shapes))] + \
-        [int(bstart[i + 1] - 1) for i in range(len(shapes))]
-    sample = workloads.sample_blocks(int(bstart[-1]), sample_count, seed, must=must)
-    which = np.searchsorted(bstart, sample, side="right") - 1
-    segs = []   # (tensor index, element start, element end, global flat start)
-    for gb, ti in zip(sample, which):
-        lb = int(gb - bstart[ti])
-        n = shapes[ti][1]
-        s, e = lb * BLOCK, min(n, (lb + 1) * BLOCK)
-        segs.append((int(ti), lb, s, e, int(offs[ti]) + s))
-    say(f"{len(segs)} sampled blocks")
+        o, bo = int(offs[ti]), int(offs[ti]) // BLOCK
+        tensors.append((P[o:o + n], G[o:o + n], CM[o:o + n], CV[o:o + n],
+                        AM[bo:bo + n // BLOCK], AV[bo:bo + n // BLOCK]))
+    nlaunch = q.qopt_adam8bit_launch_count(tensors)
+    per_launch = -(-nblk // nlaunch)
+    splits = [k * per_launch for k in range(1, nlaunch)]
+    starts = offs[:-1] // BLOCK
+    must = list(extra_blocks) + [int(b) for b in starts] + [int(b) - 1 for b in offs[1:] // BLOCK]
+    must += [b for s in splits for b in (s - 1, s)]
+    sample = workloads.sample_blocks(nblk, int(np.ceil(sample_frac * nblk)), seed, must=must)
+    assert sample.size >= sample_frac * nblk and set(must) <= set(sample.tolist())
+    say(f"{nlaunch} launches, {sample.size} sampled blocks of {nblk} "
+        f"({100.0 * sample.size / nblk:.2f} %)")
+    sidx = torch.from_numpy(sample).cuda()
 
     def gather(flat, dtype):
-        idx = torch.cat([torch.arange(f, f + (e - s), device="cuda") for _, _, s, e, f in segs])
-        return to_host(flat[idx], dtype)
+        return to_host(flat.view(-1, BLOCK)[sidx].reshape(-1), dtype)
 
-    lens = [e - s for _, _, s, e, _ in segs]
-    cuts = np.cumsum([0] + lens)
-    ref_p = gather(P, pdt)
-    ref_p = [ref_p[cuts[i]:cuts[i + 1]].copy() for i in range(len(segs))]
-    ref_s = [host_state(L) for L in lens]
+    inputs = {"p0": gather(P, pdt)}
     for step in range(1, steps + 1):
         grad_fill(G, step)
-        hg = gather(G, gdt)
+        inputs[f"g{step}"] = gather(G, gdt)
         q.qopt_adam8bit_step(tensors, step=step, **HP)
-        for i in range(len(segs)):
-            out = oracle.adam8bit_step(ref_p[i], hg[cuts[i]:cuts[i + 1]], *ref_s[i], step=step,
-                                       param_dtype=pdt, grad_dtype=gdt, **HP)
-            ref_p[i], ref_s[i] = out[0], list(out[1:])
         torch.cuda.synchronize()
         say(f"step {step} done")
+    got = [gather(CM, "u8"), gather(CV, "u8"), AM[sidx].cpu().numpy(), AV[sidx].cpu().numpy()]
     gp = gather(P, pdt)
-    for i, (ti, lb, s, e, f) in enumerate(segs):
-        st = tensors[ti]
-        got = [st[2][s:e].cpu().numpy(), st[3][s:e].cpu().numpy(),
-               st[4][lb:lb + 1].cpu().numpy(), st[5][lb:lb + 1].cpu().numpy()]
-        what = f"(tensor {shapes[ti][0]}, block {lb})"
-        assert_state(got, ref_s[i], what)
-        assert_params(gp[cuts[i]:cuts[i + 1]], ref_p[i], pdt, HP["lr"], what)
-    del tensors, P, G
+    del tensors, P, G, CM, CV, AM, AV
     torch.cuda.empty_cache()
+    cfg = dict(HP, steps=steps, pdt=pdt, gdt=gdt)
+    ref = run_oracle_blocks(inputs, cfg, sample.size, str(tmp_path))
+    assert_state(got, [ref["cm"], ref["cv"], ref["am"], ref["av"]], f"({sample.size} sampled blocks)")
+    assert_params(gp, ref["p"], pdt, HP["lr"], f"({sample.size} sampled blocks)")
 
 
 def _dense_grads(std, seed, outlier_frac=0.0, outlier_scale=1.0):
@@ -638,17 +666,17 @@ def _dense_grads(std, seed, outlier_frac=0.0, outlier_scale=1.0):
     return fill
 
 
-def test_gpt1p3b_sampled(q):
+def test_gpt1p3b_sampled(q, tmp_path):
     sampled_trajectory(q, workloads.gpt1p3b_shapes(), "f32", "bf16", steps=6, seed=2,
-                       grad_fill=_dense_grads(1e-3, 2), sample_count=1500)
+                       grad_fill=_dense_grads(1e-3, 2), tmp_path=tmp_path)
 
 
-def test_llama7b_sampled(q):
+def test_llama7b_sampled(q, tmp_path):
     sampled_trajectory(q, workloads.llama7b_shapes(), "f32", "bf16", steps=6, seed=3,
-                       grad_fill=_dense_grads(1e-3, 3, 1e-4, 1000.0), sample_count=1500)
+                       grad_fill=_dense_grads(1e-3, 3, 1e-4, 1000.0), tmp_path=tmp_path)
 
 
-def test_flat20b_sampled(q):
+def test_flat20b_sampled(q, tmp_path):
     rows, dim = workloads.FLAT20B_EMBED_ROWS, workloads.FLAT20B_EMBED_DIM
     emb = rows * dim
 
@@ -660,4 +688,4 @@ def test_flat20b_sampled(q):
 
     extra = [emb // BLOCK - 1, emb // BLOCK, 7, 1000]
     sampled_trajectory(q, [("flat", workloads.FLAT20B_N)], "bf16", "bf16", steps=3, seed=4,
-                       grad_fill=fill, sample_count=1500, extra_blocks=extra)
+                       grad_fill=fill, tmp_path=tmp_path, extra_blocks=extra)

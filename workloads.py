@@ -215,11 +215,12 @@ def zipf_token_ids(ntokens, vocab, seed, exponent=1.0):
 
 
 def sample_blocks(nblk, count, seed, must=()):
-    """Sorted block indices for sampled parity: ``must`` plus ``count`` uniform draws
-    (first and last blocks always included)."""
+    """Sorted block indices for sampled parity: ``must`` plus ``count`` distinct blocks
+    drawn uniformly without replacement (first and last blocks always included)."""
     rng = np.random.default_rng(seed)
     pick = set(int(b) for b in must if 0 <= int(b) < nblk)
-    pick.update([0, nblk - 1])
+    if nblk > 0:
+        pick.update([0, nblk - 1])
     if nblk > 0 and count > 0:
-        pick.update(int(b) for b in rng.integers(0, nblk, size=count))
+        pick.update(int(b) for b in rng.choice(nblk, size=min(int(count), nblk), replace=False))
     return np.array(sorted(pick), dtype=np.int64)
