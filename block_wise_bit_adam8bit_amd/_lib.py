@@ -18,13 +18,15 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "qopt.h")
 EMB_HEADER = os.path.join(os.path.dirname(_HERE), "include", "qopt_embedding.h")
 
 QOPT_BLOCK = 2048
-QOPT_OK, QOPT_EINVAL, QOPT_EUNSUPPORTED, QOPT_EALIGN, QOPT_ELAUNCH, QOPT_EINTERNAL = range(6)
+(QOPT_OK, QOPT_EINVAL, QOPT_EUNSUPPORTED, QOPT_EALIGN, QOPT_ELAUNCH, QOPT_EINTERNAL,
+ QOPT_ENOSPACE) = range(7)
 QOPT_CB_SIGNED, QOPT_CB_UNSIGNED = 0, 1
 QOPT_F32, QOPT_BF16 = 0, 1
 QOPT_CODEBOOK_MAGIC = 0x31424351
 QOPT_MAX_BUCKETS = 7168
 QOPT_THRESH_LEN = 272
 QOPT_EMB_VEC_MAX_DIM = 4096
+QOPT_EMB_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class QoptError(RuntimeError):
@@ -122,6 +124,14 @@ _SIGNATURES = {
                                                       ctypes.c_void_p, ctypes.c_void_p,
                                                       ctypes.c_void_p, ctypes.c_size_t,
                                                       ctypes.c_void_p]),
+    "qopt_stable_embedding_backward_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
+                                                              ctypes.c_int64, ctypes.c_int64,
+                                                              ctypes.c_void_p, ctypes.c_int64,
+                                                              ctypes.c_void_p, ctypes.c_void_p,
+                                                              ctypes.c_void_p, ctypes.c_void_p,
+                                                              ctypes.c_int, ctypes.c_void_p,
+                                                              ctypes.c_void_p, ctypes.c_void_p,
+                                                              ctypes.c_void_p]),
     "qopt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qopt_version": (ctypes.c_int, []),
 }

@@ -181,6 +181,8 @@ extern "C" const char* qopt_status_string(int status) {
     case QOPT_EALIGN: return "pointer not aligned to its element size";
     case QOPT_ELAUNCH: return "HIP launch or device query failed";
     case QOPT_EINTERNAL: return "internal invariant violated while building a codebook";
+    case QOPT_ENOSPACE:
+      return "the request needs more scratch memory than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }

@@ -1193,13 +1193,15 @@ extern "C" int qopt_stable_embedding_backward_workspace(int64_t ntokens, int64_t
   return workspace_need(ntokens, dim, cus, bytes);
 }
 
-extern "C" int qopt_stable_embedding_backward(const void* weight_dev, int weight_dtype, int64_t rows,
-                                              int64_t dim, const int64_t* idx_dev, int64_t ntokens,
-                                              const float* gamma_dev, const float* mean_dev,
-                                              const float* rstd_dev, const void* dout_dev,
-                                              int dout_dtype, float* dweight_dev, float* dgamma_dev,
-                                              float* dbeta_dev, void* workspace_dev,
-                                              size_t workspace_bytes, void* stream) {
+namespace {
+
+// The backward over a caller's workspace; `too_small` is the status returned when the
+// workspace cannot hold the shape's need.
+int backward_impl(const void* weight_dev, int weight_dtype, int64_t rows, int64_t dim,
+                  const int64_t* idx_dev, int64_t ntokens, const float* gamma_dev,
+                  const float* mean_dev, const float* rstd_dev, const void* dout_dev,
+                  int dout_dtype, float* dweight_dev, float* dgamma_dev, float* dbeta_dev,
+                  void* workspace_dev, size_t workspace_bytes, int too_small, void* stream) {
   if (rows < 0 || dim < 0 || ntokens < 0) return QOPT_EINVAL;
   if (!dtype_ok(weight_dtype) || !dtype_ok(dout_dtype)) return QOPT_EUNSUPPORTED;
   if (dim == 0) return ntokens == 0 ? QOPT_OK : QOPT_EINVAL;
@@ -1226,7 +1228,7 @@ extern "C" int qopt_stable_embedding_backward(const void* weight_dev, int weight
   size_t need = 0, level1_off = 0;
   rc = workspace_need(ntokens, dim, cus, &need, &level1_off);
   if (rc != QOPT_OK) return rc;
-  if (workspace_bytes < need) return QOPT_EINVAL;
+  if (workspace_bytes < need) return too_small;
   const bool vec = vector_ok(dim, weight_dev, weight_dtype, dout_dev, dout_dtype) &&
                    group_shape_ok(rows, dim, ntokens) && aligned(dweight_dev, 16);
   const int S = vec ? slices_for(dim) : 0;
@@ -1253,4 +1255,56 @@ extern "C" int qopt_stable_embedding_backward(const void* weight_dev, int weight
   hipLaunchKernelGGL(bwd_reduce_step2_kernel, dim3(rgrid), dim3(256), 0, s, level1, ngroups, dim,
                      dgamma_dev, dbeta_dev);
   return launch_status();
+}
+
+// Scratch of the allocation-free backward: one fixed array per device, loaded with the
+// library's device code.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in for the symbol); each device's own address is looked up
+// once, with that device current, and kept.
+__device__ __align__(256) char scratch[QOPT_EMB_STATIC_SCRATCH_BYTES];
+
+constexpr int kScratchDevices = 64;
+std::once_flag g_scratch_once[kScratchDevices];
+void* g_scratch_ptr[kScratchDevices];
+
+int device_scratch(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) return QOPT_ELAUNCH;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_ptr[dev] == nullptr) return QOPT_ELAUNCH;
+  *ptr = g_scratch_ptr[dev];
+  return QOPT_OK;
+}
+
+}  // namespace
+
+extern "C" int qopt_stable_embedding_backward(const void* weight_dev, int weight_dtype, int64_t rows,
+                                              int64_t dim, const int64_t* idx_dev, int64_t ntokens,
+                                              const float* gamma_dev, const float* mean_dev,
+                                              const float* rstd_dev, const void* dout_dev,
+                                              int dout_dtype, float* dweight_dev, float* dgamma_dev,
+                                              float* dbeta_dev, void* workspace_dev,
+                                              size_t workspace_bytes, void* stream) {
+  return backward_impl(weight_dev, weight_dtype, rows, dim, idx_dev, ntokens, gamma_dev, mean_dev,
+                       rstd_dev, dout_dev, dout_dtype, dweight_dev, dgamma_dev, dbeta_dev,
+                       workspace_dev, workspace_bytes, QOPT_EINVAL, stream);
+}
+
+extern "C" int qopt_stable_embedding_backward_noalloc(const void* weight_dev, int weight_dtype,
+                                                      int64_t rows, int64_t dim,
+                                                      const int64_t* idx_dev, int64_t ntokens,
+                                                      const float* gamma_dev, const float* mean_dev,
+                                                      const float* rstd_dev, const void* dout_dev,
+                                                      int dout_dtype, float* dweight_dev,
+                                                      float* dgamma_dev, float* dbeta_dev,
+                                                      void* stream) {
+  void* ws = nullptr;
+  const int rc = device_scratch(&ws);
+  if (rc != QOPT_OK) return rc;
+  return backward_impl(weight_dev, weight_dtype, rows, dim, idx_dev, ntokens, gamma_dev, mean_dev,
+                       rstd_dev, dout_dev, dout_dtype, dweight_dev, dgamma_dev, dbeta_dev, ws,
+                       QOPT_EMB_STATIC_SCRATCH_BYTES, QOPT_ENOSPACE, stream);
 }

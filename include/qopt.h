@@ -53,7 +53,8 @@ typedef enum {
   QOPT_EUNSUPPORTED = 2,  /* unknown dtype or codebook kind */
   QOPT_EALIGN = 3,        /* pointer not aligned to its element size */
   QOPT_ELAUNCH = 4,       /* the HIP runtime refused a launch or a device query */
-  QOPT_EINTERNAL = 5      /* codebook construction violated an internal invariant */
+  QOPT_EINTERNAL = 5,     /* codebook construction violated an internal invariant */
+  QOPT_ENOSPACE = 6       /* an allocation-free entry point's fixed scratch is too small */
 } qopt_status;
 
 /* Codebook kinds (§2 "Dynamic Quantization"). */

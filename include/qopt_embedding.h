@@ -106,6 +106,32 @@ int qopt_stable_embedding_backward(const void* weight_dev, int weight_dtype, int
                                    float* dweight_dev, float* dgamma_dev, float* dbeta_dev,
                                    void* workspace_dev, size_t workspace_bytes, void* stream);
 
+/* Bytes of device scratch the allocation-free backward holds per device (64 MiB). */
+#define QOPT_EMB_STATIC_SCRATCH_BYTES 67108864
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): qopt_stable_embedding_backward
+ * with its workspace in a fixed array of QOPT_EMB_STATIC_SCRATCH_BYTES bytes of device
+ * memory that the library holds on each device it runs on until the process ends.
+ * Same arguments, checks and results as qopt_stable_embedding_backward without the
+ * workspace; the caller still passes every input and output.  The shape's workspace
+ * need (qopt_stable_embedding_backward_workspace) must fit the array, or the call
+ * returns QOPT_ENOSPACE before enqueueing anything: at width 4096 that allows about
+ * 29,000 tokens, at width 1024 about 116,000.  The array's contents are scratch: the
+ * kernels write every part they read, so nothing needs clearing between calls.  All
+ * calls on one device share that device's array, so calls that overlap in time on
+ * one device (on different streams, or from different host threads) race; the caller
+ * orders them.  Allocates nothing: no hipMalloc, no library routine that allocates.
+ */
+int qopt_stable_embedding_backward_noalloc(const void* weight_dev, int weight_dtype,
+                                           int64_t rows, int64_t dim, const int64_t* idx_dev,
+                                           int64_t ntokens, const float* gamma_dev,
+                                           const float* mean_dev, const float* rstd_dev,
+                                           const void* dout_dev, int dout_dtype,
+                                           float* dweight_dev, float* dgamma_dev,
+                                           float* dbeta_dev, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
