@@ -296,6 +296,65 @@ def ceiling(torch, workloads, q, args):
         "step_frac_of_8TB/s": [round(a / HBM_PEAK_GBS, 4) for a, _ in rounds]}}), flush=True)
 
 
+def ceiling_study(torch, workloads, q, args):
+    """Bytes-only access patterns for the step's traffic (qopt_pattern_probe), timed
+    against the step and its own traffic probe on the same Llama-7B buffers, in a
+    shuffled order over several rounds (medians reported).  Every pattern moves the
+    step's bytes of one launch's worth of blocks per call over the whole flat set; what
+    it writes is what it read."""
+    import random
+    import statistics
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8)
+    tensors, sizes, pdt, gdt, label = make_workload("llama7b", torch, workloads)
+    prepared = q.make_tensor_array(tensors)
+    step_bytes = algorithmic_bytes(sizes, 4, 2)
+    total = sum(sizes)
+    flat = [t.as_strided((total,), (1,)) for t in tensors[0][:4]]
+    step = 0
+
+    def run_step():
+        nonlocal step
+        step += 1
+        q.qopt_adam8bit_step(tensors, step=step, _prepared=prepared, **hp)
+
+    cands = [("step", run_step),
+             ("step traffic probe", lambda: q.qopt_adam8bit_traffic_probe(tensors, _prepared=prepared))]
+    for i, name in enumerate(q.qopt_pattern_probe_names()):
+        cands.append((f"pattern {i}: {name}", lambda i=i: q.qopt_pattern_probe(i, *flat)))
+    for _ in range(5 + args.warmup):
+        run_step()
+    for _, fn in cands:
+        fn()
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return step_bytes / (e0.elapsed_time(e1) / args.steps) / 1e6
+
+    res = {name: [] for name, _ in cands}
+    rng = random.Random(0)
+    for rnd in range(5):
+        order = list(range(len(cands)))
+        rng.shuffle(order)
+        for j in order:
+            res[cands[j][0]].append(timed(cands[j][1]))
+        log(f"round {rnd} done")
+    rows = [{"what": name, "GB/s median": round(statistics.median(v), 1),
+             "GB/s min": round(min(v), 1), "GB/s max": round(max(v), 1),
+             "frac of 8 TB/s": round(statistics.median(v) / HBM_PEAK_GBS, 4)} for name, v in res.items()]
+    best = max(rows[2:], key=lambda r: r["GB/s median"])
+    print(json.dumps({"ceiling_study": {
+        "workload": label + " (flat buffers, first allocation of the process)",
+        "bytes_per_call": step_bytes, "calls_per_timing": args.steps, "rounds": 5,
+        "rows": rows, "best_pattern": best["what"], "best_frac": best["frac of 8 TB/s"],
+        "step_frac": rows[0]["frac of 8 TB/s"]}}), flush=True)
+
+
 def bench_codec(torch, workloads, q, args):
     """Block-wise quantize and dequantize of 2^28 values 0.01 * Student-t(3)."""
     n = 1 << 28
@@ -489,6 +548,9 @@ def main():
     ap.add_argument("--ceiling", action="store_true",
                     help="only time the step against the traffic probe (same bytes and access "
                          "pattern, no arithmetic) on the same buffers")
+    ap.add_argument("--ceiling-study", action="store_true",
+                    help="only time bytes-only access patterns of the step's traffic against "
+                         "the step on the Llama-7B buffers")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch copies of 4 GiB (for scaling PMC byte counters)")
     args = ap.parse_args()
@@ -510,6 +572,8 @@ def main():
         if args.workload not in ("llama7b", "gpt1p3b"):
             raise SystemExit("--placements takes the llama7b or gpt1p3b workload")
         return placements(torch, workloads, q, args)
+    if args.ceiling_study:
+        return ceiling_study(torch, workloads, q, args)
     if args.ceiling:
         if args.workload not in ("llama7b", "llama7b_shard8", "gpt1p3b", "flat20b"):
             raise SystemExit("--ceiling takes a step workload")

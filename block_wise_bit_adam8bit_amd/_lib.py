@@ -132,6 +132,11 @@ _SIGNATURES = {
                                                               ctypes.c_int, ctypes.c_void_p,
                                                               ctypes.c_void_p, ctypes.c_void_p,
                                                               ctypes.c_void_p]),
+    "qopt_pattern_probe_count": (ctypes.c_int, []),
+    "qopt_pattern_probe_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "qopt_pattern_probe": (ctypes.c_int, [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_void_p]),
     "qopt_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "qopt_version": (ctypes.c_int, []),
 }

@@ -229,3 +229,23 @@ def qopt_adam8bit_step(tensors, *, lr, beta1, beta2, eps, step, _prepared=None):
                                     _ptr(codebook(UNSIGNED, dev)), ctypes.byref(hp),
                                     ctypes.c_void_p(_lib.stream_handle(dev)))
     _lib.check("qopt_adam8bit_step", rc)
+
+
+def qopt_pattern_probe_names():
+    """Descriptions of the bytes-only access patterns (a measurement aid)."""
+    return [LIB.qopt_pattern_probe_name(i).decode() for i in range(LIB.qopt_pattern_probe_count())]
+
+
+def qopt_pattern_probe(pattern, params, grads, m_codes, v_codes):
+    """Measurement aid: one pass of access pattern ``pattern`` over flat buffers holding
+    whole blocks (fp32 params, bf16 grads, uint8 codes), every buffer left as it was."""
+    n = params.numel()
+    if n % QOPT_BLOCK or grads.numel() != n or m_codes.numel() != n or v_codes.numel() != n:
+        raise ValueError("the probe moves whole blocks of equally long flat buffers")
+    if params.dtype != torch.float32 or grads.dtype != torch.bfloat16 or \
+            m_codes.dtype != torch.uint8 or v_codes.dtype != torch.uint8:
+        raise ValueError("the probe moves fp32 params, bf16 grads and uint8 codes")
+    rc = LIB.qopt_pattern_probe(int(pattern), _ptr(params), _ptr(grads), _ptr(m_codes),
+                                _ptr(v_codes), n // QOPT_BLOCK,
+                                ctypes.c_void_p(_lib.stream_handle(params.device)))
+    _lib.check("qopt_pattern_probe", rc)

@@ -416,6 +416,28 @@ def test_traffic_probe_keeps_every_buffer(q, pdt, gdt):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
+def test_pattern_probes_keep_every_buffer(q):
+    """Every bytes-only pattern of the ceiling study writes back what it read: after
+    each, parameters, gradients and codes are bit for bit unchanged (a ragged last
+    burst of the burst patterns is left out, not corrupted)."""
+    nblk = 3 * 8 * 4 * 256 + 5       # several runs of every walk, and a partial burst
+    n = nblk * BLOCK
+    rng = np.random.default_rng(61)
+    p = torch.from_numpy(rng.normal(0, 0.02, n).astype(np.float32)).cuda()
+    g = torch.from_numpy(rng.normal(0, 1e-3, n).astype(np.float32)).cuda().bfloat16()
+    cm = torch.from_numpy(rng.integers(0, 256, n, dtype=np.uint8)).cuda()
+    cv = torch.from_numpy(rng.integers(0, 256, n, dtype=np.uint8)).cuda()
+    ref = [t.clone() for t in (p, g, cm, cv)]
+    names = q.qopt_pattern_probe_names()
+    for i, name in enumerate(names):
+        say(f"pattern probe {i}: {name}")
+        q.qopt_pattern_probe(i, p, g, cm, cv)
+        torch.cuda.synchronize()
+        for a, b in zip((p, g, cm, cv), ref):
+            assert torch.equal(a.view(torch.uint8) if a.dtype != torch.uint8 else a,
+                               b.view(torch.uint8) if b.dtype != torch.uint8 else b), name
+
+
 @pytest.mark.parametrize("pdt,gdt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "f32"),
                                      ("bf16", "bf16")])
 def test_random_hyperparameters(q, pdt, gdt):

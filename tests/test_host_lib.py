@@ -135,6 +135,24 @@ def test_bucket_table_ends_give_the_oracle_codes_of_non_finite_values(kind):
     assert int(bk[0]) == 0 and th[1] > 0
 
 
+def test_pattern_probe_host_checks():
+    """The ceiling study's bytes-only patterns: described, numbered, and their argument
+    checks answer before anything is enqueued (no GPU here)."""
+    lib = _lib.LIB
+    n = lib.qopt_pattern_probe_count()
+    assert n >= 10
+    names = [lib.qopt_pattern_probe_name(i).decode() for i in range(n)]
+    assert len(set(names)) == n and any("step's own shape" in x for x in names)
+    assert lib.qopt_pattern_probe_name(n) is None and lib.qopt_pattern_probe_name(-1) is None
+    buf = ctypes.c_void_p(16 * 1024)
+    odd = ctypes.c_void_p(16 * 1024 + 4)
+    assert lib.qopt_pattern_probe(n, buf, buf, buf, buf, 1, None) == _lib.QOPT_EINVAL
+    assert lib.qopt_pattern_probe(0, buf, buf, buf, buf, -1, None) == _lib.QOPT_EINVAL
+    assert lib.qopt_pattern_probe(0, None, buf, buf, buf, 1, None) == _lib.QOPT_EINVAL
+    assert lib.qopt_pattern_probe(0, buf, buf, odd, buf, 1, None) == _lib.QOPT_EALIGN
+    assert lib.qopt_pattern_probe(0, None, None, None, None, 0, None) == _lib.QOPT_OK
+
+
 def test_argument_checks_return_before_any_launch():
     L = qopt.LIB
     null = ctypes.c_void_p(0)
