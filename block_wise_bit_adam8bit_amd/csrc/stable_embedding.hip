@@ -1059,9 +1059,18 @@ int launch_grouped(const void* w, int64_t rows, int64_t dim, const int64_t* idx,
                      idx, ntok, static_cast<uint32_t>(rows), keys_in, vals_in);
   int rc = launch_status();
   if (rc != QOPT_OK) return rc;
+  // Keys lie in [0, rows], so only their low bit-length(rows) bits are sorted: the
+  // order is the full sort's (radix sorting is stable) with fewer digit passes.  The
+  // workspace was sized for all 32 bits, an upper bound for fewer.
+  const unsigned key_bits = 32u - static_cast<unsigned>(__builtin_clz(static_cast<uint32_t>(rows) | 1u));
+  size_t need = 0;
+  if (rocprim::radix_sort_pairs(nullptr, need, keys_in, keys, vals_in, vals,
+                                static_cast<unsigned int>(ntok), 0u, key_bits, stream) != hipSuccess)
+    return QOPT_ELAUNCH;
+  if (need > L.sort_bytes) return QOPT_EINTERNAL;
   size_t sb = L.sort_bytes;
   if (rocprim::radix_sort_pairs(ws + L.sort_tmp, sb, keys_in, keys, vals_in, vals,
-                                static_cast<unsigned int>(ntok), 0u, 32u, stream) != hipSuccess)
+                                static_cast<unsigned int>(ntok), 0u, key_bits, stream) != hipSuccess)
     return QOPT_ELAUNCH;
   const size_t lds = 3 * S * kWave * sizeof(f32x4);
   hipLaunchKernelGGL((group_chunk_kernel<S, WT, OT>), dim3(L.grid), dim3(kPairThreads),
