@@ -52,9 +52,12 @@ template <> struct StepShape<uint16_t> {
   static constexpr int kWavesPerSimd = 3;
 };
 // The step's waves walk runs of this many consecutive blocks (run r belongs to wave
-// r mod waves) rather than single blocks with a grid stride.  Each wave's streams are
-// then contiguous over two blocks; measured 1.1-1.8 % faster on the Llama-7B set.
+// r mod waves) rather than single blocks with a grid stride, so each wave's streams
+// are contiguous over the run.  Measured on the Llama-7B set: runs of two 1.1-1.8 %
+// faster than single blocks; where the step rolls its loads (step_rolls) runs of four
+// are 1.6 % faster than two (one 3.8 % slower, eight 2.4 % slower).
 constexpr uint32_t kStepRun = 2;
+constexpr uint32_t kStepRunRolled = 4;
 constexpr int kRows = static_cast<int>(sizeof(qopt_codebook) / 16);
 static_assert(kSlices * kWave * 4 == QOPT_BLOCK, "block layout");
 
@@ -475,6 +478,40 @@ template <typename PT, int kMode> constexpr int step_waves() {
 template <typename PT, typename GT> constexpr bool step_rolls() {
   return std::is_same<PT, float>::value && std::is_same<GT, uint16_t>::value;
 }
+template <typename PT, typename GT> constexpr uint32_t step_run() {
+  return step_rolls<PT, GT>() ? kStepRunRolled : kStepRun;
+}
+
+// The blocks one wave of the step takes, in order: runs of kRun consecutive blocks,
+// run r on wave r mod (number of waves), over the largest prefix of the launch in
+// which every wave gets the same number of runs; then the remaining blocks one at a
+// time, block full + j on wave j mod (number of waves).  Every block is taken exactly
+// once, and the launch's last round no longer leaves some waves a whole run behind the
+// others.  (All wave-uniform, in scalar registers.)
+template <uint32_t kRun> struct StepWalk {
+  uint32_t full;     // blocks in whole rounds of runs
+  uint32_t stride;   // waves in the grid
+  uint32_t wave_id;  // this wave's index in the grid
+  __device__ StepWalk(uint32_t total, uint32_t waves, uint32_t id) : stride(waves), wave_id(id) {
+    const uint64_t round = static_cast<uint64_t>(waves) * kRun;
+    full = static_cast<uint32_t>(total / round * round);
+  }
+  __device__ uint32_t first() const {
+    const uint64_t b = static_cast<uint64_t>(wave_id) * kRun;
+    return b < full ? static_cast<uint32_t>(b) : full + wave_id;
+  }
+  // the block after b, or a value >= every launch's block count (2^32 - 1 at most)
+  __device__ uint32_t next(uint32_t b) const {
+    uint64_t nb;
+    if (b < full) {
+      nb = ((b + 1) % kRun) ? uint64_t{b} + 1 : (uint64_t{b / kRun} + stride) * kRun;
+      if (nb >= full) nb = uint64_t{full} + wave_id;
+    } else {
+      nb = uint64_t{b} + stride;
+    }
+    return nb > 0xFFFFFFFFu ? 0xFFFFFFFFu : static_cast<uint32_t>(nb);
+  }
+};
 
 // One launch's work: up to kMaxTensors pieces, each a run of whole blocks of one
 // tensor.  Large tensors may be split over several launches so that every launch
@@ -906,11 +943,11 @@ __device__ __forceinline__ void requantize(const Encoder& em, const Encoder& ev,
   }
 }
 
-// Each wave walks runs of kStepRun consecutive blocks, one run per grid stride of
-// runs.  While it requantizes one block,
-// the vector inputs of its next block are already in flight (loaded into the
-// registers the update no longer needs), so memory stays busy through the
-// requantization phase.
+// Each wave walks its blocks in StepWalk's order (runs of step_run() consecutive
+// blocks, then single blocks for the launch's remainder).  While it requantizes one
+// block, the vector inputs of its next block are already in flight: loaded into the
+// registers the update no longer needs, slice by slice during the update where the
+// step rolls (step_rolls), else all at once after it.
 template <typename PT, typename GT, int kMode>
 __global__ void __launch_bounds__(kThreads, (step_waves<PT, kMode>()))
 adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qopt_codebook* cbv_g) {
@@ -930,7 +967,8 @@ adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qo
   const uint32_t total = c.block_start[c.npieces];
   float* vstash = kVInLds ? vstash_all + wave * QOPT_BLOCK : vstash_all;
 
-  uint32_t blk = (blockIdx.x * kWaves + wave) * kStepRun;
+  const StepWalk<step_run<PT, GT>()> walk(total, stride, blockIdx.x * kWaves + wave);
+  uint32_t blk = walk.first();
   if (blk >= total) return;
   BlockRef cur = resolve(c, blk);
   BlockIn<PT, GT> in;
@@ -938,8 +976,7 @@ adam8bit_kernel(StepChunk c, AdamScalars k, const qopt_codebook* cbm_g, const qo
   for (;;) {
     float m[kSlices][4], v[kSlices][4];
     float mmax = 0.0f, vmax = 0.0f;
-    // the next block of this run, else the first block of the wave's next run
-    const uint32_t nblk = ((blk + 1) % kStepRun) ? blk + 1 : (blk / kStepRun + stride) * kStepRun;
+    const uint32_t nblk = walk.next(blk);
     const bool more = nblk < total;
     const BlockRef nxt = more ? resolve(c, nblk) : cur;
     const bool next_vec = more && nxt.vec;
@@ -984,7 +1021,8 @@ __global__ void __launch_bounds__(kThreads) step_traffic_kernel(StepChunk c) {
   const int lane = threadIdx.x % kWave;
   const uint32_t stride = gridDim.x * kWaves;
   const uint32_t total = c.block_start[c.npieces];
-  uint32_t blk = (blockIdx.x * kWaves + wave) * kStepRun;
+  const StepWalk<step_run<PT, GT>()> walk(total, stride, blockIdx.x * kWaves + wave);
+  uint32_t blk = walk.first();
   if (blk >= total) return;
   BlockRef cur = resolve(c, blk);
   BlockIn<PT, GT> in;
@@ -992,7 +1030,7 @@ __global__ void __launch_bounds__(kThreads) step_traffic_kernel(StepChunk c) {
   for (;;) {
     uint32_t cm[kSlices], cv[kSlices];
     float am = 0.0f, av = 0.0f;
-    const uint32_t nblk = ((blk + 1) % kStepRun) ? blk + 1 : (blk / kStepRun + stride) * kStepRun;
+    const uint32_t nblk = walk.next(blk);
     const bool more = nblk < total;
     const BlockRef nxt = more ? resolve(c, nblk) : cur;
     const bool next_vec = more && nxt.vec;
@@ -1243,7 +1281,7 @@ template <typename PT, typename GT, int kMode>
 int launch_step_mode(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size_t gsize,
                      const AdamScalars& k, const qopt_codebook* cbm, const qopt_codebook* cbv,
                      hipStream_t stream) {
-  return launch_planned<StepChunk>(adam8bit_kernel<PT, GT, kMode>, 0, kStepRun, ntensors,
+  return launch_planned<StepChunk>(adam8bit_kernel<PT, GT, kMode>, 0, step_run<PT, GT>(), ntensors,
                                    StepSize{tensors}, StepFill{tensors, psize, gsize}, stream, k,
                                    cbm, cbv);
 }
@@ -1451,7 +1489,7 @@ int launch_traffic_probe(const qopt_tensor* tensors, int32_t ntensors, size_t ps
   int per_cu = 0;
   const int rc = step_wg_per_cu<PT, GT>(&per_cu);
   if (rc != QOPT_OK) return rc;
-  return launch_planned<StepChunk>(step_traffic_kernel<PT, GT>, per_cu, kStepRun, ntensors,
+  return launch_planned<StepChunk>(step_traffic_kernel<PT, GT>, per_cu, step_run<PT, GT>(), ntensors,
                                    StepSize{tensors}, StepFill{tensors, psize, gsize}, stream);
 }
 

@@ -688,6 +688,18 @@ def _dense_grads(std, seed, outlier_frac=0.0, outlier_scale=1.0):
     return fill
 
 
+@pytest.mark.parametrize("pdt,gdt", [("f32", "bf16"), ("bf16", "bf16"), ("f32", "f32")])
+def test_every_block_of_long_launches(q, pdt, gdt, tmp_path):
+    """Launches long enough for every wave to take several whole runs of consecutive
+    blocks, with remainders that do not fill a round, and a second tensor whose
+    launch is short: every block (the runs, the single blocks after them, the short
+    launch's) is followed through two steps in the oracle, so a block the walk skips
+    or takes twice cannot pass."""
+    shapes = [("long", (3 * 8192 + 777) * BLOCK), ("short", 301 * BLOCK)]
+    sampled_trajectory(q, shapes, pdt, gdt, steps=2, seed=23, grad_fill=_dense_grads(1e-3, 23),
+                       tmp_path=tmp_path, sample_frac=1.0)
+
+
 def test_gpt1p3b_sampled(q, tmp_path):
     sampled_trajectory(q, workloads.gpt1p3b_shapes(), "f32", "bf16", steps=6, seed=2,
                        grad_fill=_dense_grads(1e-3, 2), tmp_path=tmp_path)
