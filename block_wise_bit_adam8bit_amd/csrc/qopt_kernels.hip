@@ -38,7 +38,7 @@ constexpr int kSlices = QOPT_BLOCK / (kWave * 4);  // 8 slices of 4 elements per
 constexpr int kMaxTensors = 48;                 // tensors per launch (kernarg budget)
 // Where the step keeps a block's second moments until the block maximum is known.
 // With fp32 parameters a lane holds its 32 m and 32 v values plus the prefetched
-// inputs of the next block in registers: about 240 VGPRs, 2 waves per SIMD.  With
+// inputs of the next block in registers: 218-246 VGPRs, 2 waves per SIMD.  With
 // bf16 parameters the inputs are smaller and v waits in the wave's own 8 KB of LDS
 // instead (written slice by slice after its last use in the update, read back slice
 // by slice when encoding), which brings the kernel under 168 VGPRs: 3 waves per
