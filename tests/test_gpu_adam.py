@@ -190,6 +190,34 @@ def test_misaligned_views(q):
 
 
 @pytest.mark.parametrize("pdt,gdt", [("f32", "bf16"), ("bf16", "bf16")])
+def test_misaligned_pieces_inside_runs(q, pdt, gdt):
+    """One launch of more blocks than the grid's waves take in whole runs, in which
+    tensors that must take the element-wise path (parameters at odd element offsets)
+    sit between aligned ones, so that runs of consecutive blocks pass from vector
+    blocks to element-wise ones and back, and the next block a wave loads ahead is
+    sometimes not a vector block."""
+    sizes = [5 * 2048 + 11, 4000 * 2048, 2049, 4200 * 2048, 7]
+    odd = {0, 2, 4}
+    elt = torch.float32 if pdt == "f32" else torch.bfloat16
+
+    def views(hp_p):
+        tot = sum(sizes) + 2048 * len(sizes)
+        pbuf = torch.zeros(tot, dtype=elt, device="cuda")
+        dp, ds, off = [], [], 0
+        for i, (p, n) in enumerate(zip(hp_p, sizes)):
+            start = off + (1 if i in odd else 0)
+            v = pbuf[start:start + n]
+            v.copy_(to_dev(p, pdt))
+            dp.append(v)
+            ds.append(dev_state(n))
+            off += -(-(n + 1) // 2048) * 2048
+        return dp, ds
+
+    say(f"misaligned pieces inside runs {pdt}/{gdt}")
+    run_small(q, sizes, pdt, gdt, steps=2, seed=29, views=views)
+
+
+@pytest.mark.parametrize("pdt,gdt", [("f32", "bf16"), ("bf16", "bf16")])
 def test_rank_shares_step_independently(q, pdt, gdt):
     """Three ranks' shares (contiguous ranges of whole blocks of the flattened tensors,
     each stepped by its own call on views of the full tensors and block maxima) give
