@@ -568,6 +568,47 @@ def test_optimizer_class_and_resume(q):
     assert torch.equal(w.detach(), final_w) and torch.equal(b.detach(), final_b)
 
 
+def _busy(stream, n=4096, reps=12):
+    """Queue several milliseconds of matrix products on ``stream``."""
+    with torch.cuda.stream(stream):
+        a = torch.full((n, n), 1.0 / n, device="cuda")  # a @ a == a
+        for _ in range(reps):
+            a = a @ a
+    return a
+
+
+def test_step_runs_on_the_callers_stream(q):
+    """The step goes on the caller's current stream: on a side stream (default
+    priority) queued behind long matrix products and the copy that fills the
+    gradients, it must see those gradients, and its results must equal the oracle's.
+    A step queued anywhere else would read the zero gradients the copy overwrites."""
+    rng = np.random.default_rng(2024)
+    sizes = [3 * BLOCK + 5, 40 * BLOCK]
+    pdt, gdt = "f32", "bf16"
+    hp_p = [host_params(n, pdt, rng) for n in sizes]
+    hg = [host_grads(n, gdt, rng) for n in sizes]
+    dp = [to_dev(p, pdt) for p in hp_p]
+    ds = [dev_state(n) for n in sizes]
+    src = [to_dev(g, gdt) for g in hg]
+    dg = [torch.zeros_like(t) for t in src]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    say(f"side stream step sizes={sizes}")
+    _busy(side)
+    with torch.cuda.stream(side):
+        for d, g in zip(dg, src):
+            d.copy_(g)
+        q.qopt_adam8bit_step([(dp[i], dg[i], *ds[i]) for i in range(len(sizes))], step=1, **HP)
+    side.synchronize()
+    for i, n in enumerate(sizes):
+        hs = host_state(n)
+        out = oracle.adam8bit_step(hp_p[i], hg[i], *hs, step=1, param_dtype=pdt, grad_dtype=gdt,
+                                   **HP)
+        what = f"(tensor {i}, n={n}, side stream)"
+        assert_state([t.cpu().numpy() for t in ds[i]], list(out[1:]), what)
+        assert_params(to_host(dp[i], pdt), out[0], pdt, HP["lr"], what)
+
+
 def test_optimizer_per_parameter_steps(q):
     """A parameter without a gradient skips the step and keeps its own step count
     (as torch.optim.Adam does); the parameters then fall into separate launches per

@@ -70,6 +70,32 @@ def test_block_max_at_every_position(q, kind):
     _check_codec(q, x, kind)
 
 
+def test_codec_runs_on_the_callers_stream(q):
+    """Quantize and dequantize go on the caller's current stream: on a side stream
+    (default priority) queued behind long matrix products and the copy that fills
+    their input, they must see that input, and their outputs must equal the oracle's."""
+    kind = oracle.SIGNED
+    x = workloads.student_t3_host(5 * 2048 + 77, seed=31)
+    src = torch.from_numpy(x).cuda()
+    xd = torch.zeros_like(src)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    say(f"side stream codec n={x.size}")
+    with torch.cuda.stream(side):
+        a = torch.full((4096, 4096), 1.0 / 4096, device="cuda")  # a @ a == a
+        for _ in range(12):
+            a = a @ a
+        xd.copy_(src)
+        c, m = q.qopt_quantize_blockwise(xd, kind)
+        y = q.qopt_dequantize_blockwise(c, m, kind)
+    side.synchronize()
+    c_ref, a_ref = oracle.quantize_blockwise(x, kind)
+    y_ref = oracle.dequantize_blockwise(c_ref, a_ref, kind)
+    assert np.array_equal(c.cpu().numpy(), c_ref)
+    assert np.array_equal(m.cpu().numpy().view(np.uint32), a_ref.view(np.uint32))
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), y_ref.view(np.uint32))
+
+
 @pytest.mark.parametrize("kind", KINDS)
 def test_codec_misaligned_views(q, kind):
     """Views at element offsets that break 16-byte (x) and 4-byte (codes) alignment
