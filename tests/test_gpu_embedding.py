@@ -191,6 +191,39 @@ def test_misaligned_views_take_the_element_path(q):
     assert_within(host(out), y, tol, "forward output (unaligned table)")
 
 
+def test_runs_on_the_callers_stream(q):
+    """Forward and backward go on the caller's current stream: on a side stream
+    (default priority) queued behind long matrix products and the copies that fill
+    their inputs, they must see those inputs and give the same bits as on the default
+    stream (both passes are deterministic)."""
+    rows, dim, ntok = 300, 2048, 1500
+    w_h, idx_h, g_h, b_h = _inputs(rows, dim, ntok, 91)[:4]
+    w, gamma, beta = to_dev(w_h, "f32"), to_dev(g_h, "f32"), to_dev(b_h, "f32")
+    idx = torch.from_numpy(idx_h).cuda()
+    dy_h = np.random.default_rng(92).normal(0.0, 1.0, (ntok, dim)).astype(np.float32)
+    dy = to_dev(dy_h, "bf16")
+    out0, mean0, rstd0 = q.qopt_stable_embedding_forward(w, idx, gamma, beta, out_dtype=torch.bfloat16)
+    dw0, dg0, db0 = q.qopt_stable_embedding_backward(w, idx, gamma, mean0, rstd0, dy)
+    torch.cuda.synchronize()
+    idx_s, dy_s = torch.zeros_like(idx), torch.zeros_like(dy)
+    side = torch.cuda.Stream()
+    say(f"side stream embedding rows={rows} dim={dim} ntok={ntok}")
+    with torch.cuda.stream(side):
+        a = torch.full((4096, 4096), 1.0 / 4096, device="cuda")  # a @ a == a
+        for _ in range(12):
+            a = a @ a
+        idx_s.copy_(idx)
+        dy_s.copy_(dy)
+        out1, mean1, rstd1 = q.qopt_stable_embedding_forward(w, idx_s, gamma, beta,
+                                                             out_dtype=torch.bfloat16)
+        dw1, dg1, db1 = q.qopt_stable_embedding_backward(w, idx_s, gamma, mean1, rstd1, dy_s)
+    side.synchronize()
+    for nm, x0, x1 in [("out", out0, out1), ("mean", mean0, mean1), ("rstd", rstd0, rstd1),
+                       ("dweight", dw0, dw1), ("dgamma", dg0, dg1), ("dbeta", db0, db1)]:
+        assert torch.equal(x0.view(torch.int16) if x0.dtype == torch.bfloat16 else x0.view(torch.int32),
+                           x1.view(torch.int16) if x1.dtype == torch.bfloat16 else x1.view(torch.int32)), nm
+
+
 def test_bad_indices_and_empty_batches(q):
     rows, dim = 16, 512
     w, _, gamma, beta, _ = _inputs(rows, dim, 4, seed=10)
