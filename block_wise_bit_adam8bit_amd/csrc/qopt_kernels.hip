@@ -13,7 +13,8 @@
 //   * A block's absmax is a max over the lane's 32 values then a DPP reduction across
 //     the wave: no LDS, no barrier, no other wave involved.
 //   * Workgroups of 4 waves are persistent: each stages the codebook(s) into LDS once
-//     (the only barrier) and then walks blocks with a grid stride.
+//     (the only barrier) and then walks blocks: the codec with a grid stride, the step
+//     in runs of consecutive blocks per wave (StepWalk).
 //   * Code lookup: decode is one LDS read; encode is one LDS byte read (bucket index
 //     from the binary32 bits) plus one LDS threshold read and a compare.
 // Floating point: compiled with -ffp-contract=off; '/' and sqrtf are the correctly
