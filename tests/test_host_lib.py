@@ -225,6 +225,33 @@ def test_launch_plan_host_only(shapes, want):
     assert qopt.LIB.qopt_adam8bit_launch_count(arr, 1, 0, 0, None) == qopt.QOPT_EINVAL
 
 
+def test_host_calls_from_many_threads():
+    """The host entry points keep no shared mutable state: 16 threads building both
+    codebooks and planning launches at once (ctypes releases the GIL during each call)
+    get exactly the single-threaded results."""
+    from concurrent.futures import ThreadPoolExecutor
+    import workloads
+    L = qopt.LIB
+    sizes = [n for _, n in workloads.llama7b_shapes()]
+    arr = _fake_tensors(sizes)
+    ref = {k: bytes(qopt.qopt_codebook_build(k)) for k in (oracle.SIGNED, oracle.UNSIGNED)}
+
+    def work(i):
+        out = []
+        for r in range(40):
+            kind = (i + r) % 2
+            cb = _lib.qopt_codebook()
+            assert L.qopt_codebook_build(kind, ctypes.byref(cb)) == qopt.QOPT_OK
+            out.append(bytes(cb) == ref[kind])
+            n = ctypes.c_int64(-1)
+            assert L.qopt_adam8bit_launch_count(arr, len(sizes), 0, 1, ctypes.byref(n)) == 0
+            out.append(n.value == 7)
+        return all(out)
+
+    with ThreadPoolExecutor(16) as ex:
+        assert all(ex.map(work, range(16)))
+
+
 def test_multi_codec_argument_checks():
     L = qopt.LIB
     C = _lib.qopt_codec_tensor
