@@ -609,6 +609,51 @@ def test_step_runs_on_the_callers_stream(q):
         assert_params(to_host(dp[i], pdt), out[0], pdt, HP["lr"], what)
 
 
+def test_steps_from_two_threads_on_two_streams(q):
+    """Two host threads step two disjoint tensor sets at once, each on its own stream
+    (default priority): the library keeps no per-call state, so both match the oracle."""
+    import threading
+    sizes = {"a": [5 * BLOCK + 3, 17 * BLOCK], "b": [BLOCK - 1, 23 * BLOCK + 100]}
+    pdt, gdt = "f32", "bf16"
+    rng = np.random.default_rng(4242)
+    hp_p = {k: [host_params(n, pdt, rng) for n in v] for k, v in sizes.items()}
+    hg = {k: [[host_grads(n, gdt, rng) for n in v] for _ in range(3)] for k, v in sizes.items()}
+    dp = {k: [to_dev(p, pdt) for p in hp_p[k]] for k in sizes}
+    ds = {k: [dev_state(n) for n in v] for k, v in sizes.items()}
+    dg = {k: [[to_dev(g, gdt) for g in step] for step in hg[k]] for k in sizes}
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(k):
+        try:
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for step in range(1, 4):
+                    q.qopt_adam8bit_step([(dp[k][i], dg[k][step - 1][i], *ds[k][i])
+                                          for i in range(len(sizes[k]))], step=step, **HP)
+            stream.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    say(f"two threads, sizes={sizes}")
+    threads = [threading.Thread(target=run, args=(k,)) for k in sizes]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for k, v in sizes.items():
+        for i, n in enumerate(v):
+            p, st = hp_p[k][i], host_state(n)
+            for step in range(1, 4):
+                out = oracle.adam8bit_step(p, hg[k][step - 1][i], *st, step=step, param_dtype=pdt,
+                                           grad_dtype=gdt, **HP)
+                p, st = out[0], list(out[1:])
+            what = f"(set {k}, tensor {i}, n={n})"
+            assert_state([t.cpu().numpy() for t in ds[k][i]], st, what)
+            assert_params(to_host(dp[k][i], pdt), p, pdt, HP["lr"], what)
+
+
 def test_optimizer_per_parameter_steps(q):
     """A parameter without a gradient skips the step and keeps its own step count
     (as torch.optim.Adam does); the parameters then fall into separate launches per
