@@ -249,6 +249,34 @@ def test_full_size_student_t(q, kind):
     torch.cuda.empty_cache()
 
 
+def test_codec_past_32_bit_element_offsets(q):
+    """One tensor of 2^32 + 3 * 2048 + 77 values (signed codebook), so that element
+    offsets pass 2^31 and 2^32 and the last block is short: blocks on either side of
+    both boundaries, the tail block and a random sample against the oracle."""
+    kind = oracle.SIGNED
+    n = (1 << 32) + 3 * 2048 + 77
+    nblk = -(-n // 2048)
+    say(f"codec past 32-bit offsets n={n}")
+    x = torch.empty(n, dtype=torch.float32, device="cuda")
+    workloads.student_t3_(x, seed=9)
+    codes, absmax = q.qopt_quantize_blockwise(x, kind)
+    y = q.qopt_dequantize_blockwise(codes, absmax, kind)
+    b31, b32 = (1 << 31) // 2048, (1 << 32) // 2048
+    must = [0, b31 - 1, b31, b32 - 1, b32, nblk - 2, nblk - 1]
+    for b in workloads.sample_blocks(nblk, 200, seed=3, must=must):
+        b = int(b)
+        lo, hi = b * 2048, min(n, b * 2048 + 2048)
+        xs = x[lo:hi].cpu().numpy()
+        c_ref, a_ref = oracle.quantize_blockwise(xs, kind)
+        assert np.array_equal(codes[lo:hi].cpu().numpy(), c_ref), f"block {b}"
+        assert absmax[b].item() == a_ref[0], f"block {b}"
+        assert np.array_equal(y[lo:hi].cpu().numpy().view(np.uint32),
+                              oracle.dequantize_blockwise(c_ref, a_ref, kind).view(np.uint32)), \
+            f"block {b}"
+    del x, codes, absmax, y
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("kind", KINDS)
 def test_multi_tensor_codec_matches_oracle(q, kind):
     """Many tensors (ragged tails, empty ones, misaligned views, more than 48 of them)
