@@ -802,6 +802,17 @@ def _dense_grads(std, seed, outlier_frac=0.0, outlier_scale=1.0):
     return fill
 
 
+def test_fp32_step_past_32_bit_element_offsets(q, tmp_path):
+    """One fp32-parameter tensor of 2^32 + 5 * 2048 elements with bf16 gradients, so
+    that element offsets pass 2^31 and 2^32 inside one tensor (and inside one
+    launch): the blocks on either side of both boundaries and a sample of the rest
+    through two steps, against the oracle."""
+    b31, b32 = (1 << 31) // BLOCK, (1 << 32) // BLOCK
+    sampled_trajectory(q, [("huge", (1 << 32) + 5 * BLOCK)], "f32", "bf16", steps=2, seed=6,
+                       grad_fill=_dense_grads(1e-3, 6, 1e-4, 1000.0), tmp_path=tmp_path,
+                       sample_frac=0.0005, extra_blocks=[b31 - 1, b31, b32 - 1, b32])
+
+
 @pytest.mark.parametrize("pdt,gdt", [("f32", "bf16"), ("bf16", "bf16"), ("f32", "f32")])
 def test_every_block_of_long_launches(q, pdt, gdt, tmp_path):
     """Launches long enough for every wave to take several whole runs of consecutive
