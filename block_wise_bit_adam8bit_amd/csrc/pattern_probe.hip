@@ -17,6 +17,7 @@ constexpr int kWave = 64;
 constexpr int kWaves = 4;  // waves per workgroup: one per SIMD
 constexpr int kThreads = kWave * kWaves;
 constexpr int kSlices = 8;  // 1 KB parameter accesses per block (16 B per lane)
+constexpr uint64_t kMaxLaunchBlocks = uint64_t{1} << 18;  // blocks per launch at most
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -275,8 +276,17 @@ extern "C" int qopt_pattern_probe(int pattern, void* params, void* grads, uint8_
   // one 4-wave workgroup per CU per wave and SIMD, as the pattern's registers allow
   const Pattern& pt = kPatterns[pattern];
   const unsigned grid = static_cast<unsigned>(cus * pt.waves_per_simd);
-  const Bufs b{static_cast<u32x4*>(params), static_cast<u32x2*>(grads), m_codes, v_codes,
-               static_cast<uint64_t>(nblocks)};
-  hipLaunchKernelGGL(pt.kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream), b);
-  return hipGetLastError() == hipSuccess ? QOPT_OK : QOPT_ELAUNCH;
+  // launches of equal block counts, at most 2^18 blocks each, as the step plans its own
+  const uint64_t total = static_cast<uint64_t>(nblocks);
+  const uint64_t nlaunch = (total + kMaxLaunchBlocks - 1) / kMaxLaunchBlocks;
+  const uint64_t per = (total + nlaunch - 1) / nlaunch;
+  for (uint64_t b0 = 0; b0 < total; b0 += per) {
+    const uint64_t nb = total - b0 < per ? total - b0 : per;
+    const Bufs b{static_cast<u32x4*>(params) + b0 * 512, static_cast<u32x2*>(grads) + b0 * 512,
+                 m_codes + b0 * 2048, v_codes + b0 * 2048, nb};
+    hipLaunchKernelGGL(pt.kernel, dim3(grid), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                       b);
+    if (hipGetLastError() != hipSuccess) return QOPT_ELAUNCH;
+  }
+  return QOPT_OK;
 }

@@ -1188,8 +1188,18 @@ int plan_chunks(int32_t ntensors, const SizeOf& size_of, const Fill& fill, uint6
   return QOPT_OK;
 }
 
-// Launch count of the plan: the smallest count (from the piece bound up) whose
-// greedy assignment keeps every launch within kMaxTensors pieces and 2^31 blocks.
+// Blocks per launch at most.  Every wave of a launch takes the same number of blocks,
+// but waves progress at different rates, so over a long launch they drift apart and
+// the blocks in flight spread over an ever wider stretch of memory.  Measured in one
+// process on the same buffers, against one launch per 48 tensors: the Llama-7B step
+// 1.5 % faster with launches of at most 2^18 blocks (1.1 % at 2^17, 2.6 % slower at
+// 2^15, where the launches' ramps and tails start to cost), the 20B bf16 step 2.1 %
+// faster (its single launch became 38), the codec on one 6.7e9-value tensor 2-4 %.
+constexpr uint64_t kMaxLaunchBlocks = uint64_t{1} << 18;
+
+// Launch count of the plan: the smallest count (from the piece and block bounds up)
+// whose greedy assignment keeps every launch within kMaxTensors pieces and
+// kMaxLaunchBlocks blocks.
 template <typename Chunk, typename SizeOf, typename Fill>
 int count_chunks(int32_t ntensors, const SizeOf& size_of, const Fill& fill,
                  uint64_t* nchunks_out, uint64_t* total_out) {
@@ -1206,7 +1216,7 @@ int count_chunks(int32_t ntensors, const SizeOf& size_of, const Fill& fill,
   *nchunks_out = 0;
   if (total == 0) return QOPT_OK;
   uint64_t nchunks = (pieces + kMaxTensors - 1) / kMaxTensors;
-  const uint64_t by_size = (total + 0x7FFFFFFFull - 1) / 0x7FFFFFFFull;
+  const uint64_t by_size = (total + kMaxLaunchBlocks - 1) / kMaxLaunchBlocks;
   if (nchunks < by_size) nchunks = by_size;
   for (;; ++nchunks) {
     bool fits = false;

@@ -153,8 +153,8 @@ typedef struct qopt_codec_tensor {
 /*
  * Multi-tensor forms of qopt_quantize_blockwise / qopt_dequantize_blockwise: the same
  * per-block results for every tensor of the host array `tensors`, in launches of equal
- * block counts with at most 48 tensor pieces each (as for qopt_adam8bit_step) instead
- * of one launch per tensor.  This is the moment codec of optimizer checkpoints (the
+ * block counts with at most 48 tensor pieces and 2^18 blocks each (as for
+ * qopt_adam8bit_step) instead of one launch per tensor.  This is the moment codec of optimizer checkpoints (the
  * checkpoint-compression page, ExCP: momentum stored as a codebook plus per-element
  * indices).  Checks: tensors != NULL when ntensors > 0, ntensors >= 0, every n >= 0,
  * non-null pointers for n > 0, alignment as above; tensors with n == 0 are skipped.
@@ -224,8 +224,9 @@ int qopt_adam8bit_step(const qopt_tensor* tensors, int32_t ntensors, int param_d
 /*
  * Number of kernel launches qopt_adam8bit_step enqueues for this tensor list and
  * these dtypes (host only, nothing is launched): the step is split into launches of
- * equal block counts holding at most 48 tensor pieces each.  Same argument checks as
- * qopt_adam8bit_step for the tensors and dtypes; *launches is host memory.
+ * equal block counts holding at most 48 tensor pieces and 2^18 blocks each.  Same
+ * argument checks as qopt_adam8bit_step for the tensors and dtypes; *launches is host
+ * memory.
  */
 int qopt_adam8bit_launch_count(const qopt_tensor* tensors, int32_t ntensors, int param_dtype,
                                int grad_dtype, int64_t* launches);

@@ -35,7 +35,8 @@ const char* qopt_pattern_probe_name(int pattern);
 /*
  * Moves the bytes described above once over `nblocks` blocks of the flat buffers
  * (device memory, each 16-byte aligned): params 2048 * nblocks fp32, grads 2048 *
- * nblocks bf16, m_codes and v_codes 2048 * nblocks bytes.  Enqueued on `stream`.
+ * nblocks bf16, m_codes and v_codes 2048 * nblocks bytes.  Enqueued on `stream`, in
+ * launches of equal block counts holding at most 2^18 blocks each (as the step's).
  * Errors: QOPT_EINVAL (pattern out of range, NULL pointer with nblocks > 0, nblocks
  * < 0), QOPT_EALIGN, QOPT_ELAUNCH.  nblocks == 0 is a no-op.
  */

@@ -131,7 +131,7 @@ def test_host_code_under_sanitizers(driver):
         want.append((rc, n if rc == 0 else -1))
     got = [(rc, n if rc == 0 else -1) for rc, n in got]
     assert got == want
-    assert want[0] == (0, 7)                           # the Llama-7B set: seven launches
+    assert want[0] == (0, 13)                          # the Llama-7B set: thirteen launches
     assert want[-2][0] == qopt.QOPT_EINVAL and want[-1][0] == qopt.QOPT_EUNSUPPORTED
 
 
