@@ -154,7 +154,8 @@ typedef struct qopt_codec_tensor {
  * Multi-tensor forms of qopt_quantize_blockwise / qopt_dequantize_blockwise: the same
  * per-block results for every tensor of the host array `tensors`, in launches of equal
  * block counts with at most 48 tensor pieces and 2^18 blocks each (as for
- * qopt_adam8bit_step) instead of one launch per tensor.  This is the moment codec of optimizer checkpoints (the
+ * qopt_adam8bit_step; calls of more than 2^18 blocks in launches of at most 2^16)
+ * instead of one launch per tensor.  This is the moment codec of optimizer checkpoints (the
  * checkpoint-compression page, ExCP: momentum stored as a codebook plus per-element
  * indices).  Checks: tensors != NULL when ntensors > 0, ntensors >= 0, every n >= 0,
  * non-null pointers for n > 0, alignment as above; tensors with n == 0 are skipped.
