@@ -1101,6 +1101,26 @@ int current_cus(int* cus) {
   return QOPT_OK;
 }
 
+// A second stream per device, created on first use and kept until the process ends
+// (default priority, non-blocking), over which the bf16-parameter step spreads its
+// launches (launch_planned).
+std::once_flag g_side_once[kMaxDevices];
+hipStream_t g_side[kMaxDevices];
+int g_side_rc[kMaxDevices];
+
+int side_stream(hipStream_t* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QOPT_ELAUNCH;
+  std::call_once(g_side_once[dev], [dev] {
+    g_side_rc[dev] = hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking) == hipSuccess
+                         ? QOPT_OK
+                         : QOPT_ELAUNCH;
+  });
+  if (g_side_rc[dev] != QOPT_OK) return g_side_rc[dev];
+  *out = g_side[dev];
+  return QOPT_OK;
+}
+
 // Persistent grid: enough workgroups to fill every CU at the kernel's occupancy
 // (or at most cap per CU, if cap > 0), never more than there are blocks to hand out.
 // Each wave of the kernel takes `run` consecutive blocks at a time.
@@ -1242,23 +1262,61 @@ int count_chunks(int32_t ntensors, const SizeOf& size_of, const Fill& fill,
 }
 
 // Plans and launches `kernel` over the tensors, one launch per chunk of the plan.
-template <typename Chunk, typename Kernel, typename SizeOf, typename Fill, typename... Args>
+// kFork: the launches alternate between `stream` and the device's second stream
+// (side_stream), so that each launch's last waves overlap the next launch's first
+// ones; the second stream starts after the work queued on `stream` before the call,
+// and `stream` waits for the second stream's launches before anything queued after
+// the call.  The launches touch disjoint blocks, so their order does not matter.
+// Measured in one process on the same buffers: the 20B bf16 step (38 launches) 4.9 %
+// faster in two processes; the fp32-parameter steps 1-1.6 % slower, so they keep one
+// stream.
+template <typename Chunk, bool kFork = false, typename Kernel, typename SizeOf, typename Fill,
+          typename... Args>
 int launch_planned(Kernel kernel, int cap, uint32_t run, int32_t ntensors, const SizeOf& size_of,
                    const Fill& fill, hipStream_t stream, Args... args) {
   uint64_t nchunks = 0, total = 0;
   int rc = count_chunks<Chunk>(ntensors, size_of, fill, &nchunks, &total);
   if (rc != QOPT_OK || total == 0) return rc;
+  hipStream_t second = stream;
+  hipEvent_t before = nullptr, after = nullptr;
+  const bool fork = kFork && nchunks > 1;
+  if (fork) {
+    rc = side_stream(&second);
+    if (rc != QOPT_OK) return rc;
+    if (hipEventCreateWithFlags(&before, hipEventDisableTiming) != hipSuccess) return QOPT_ELAUNCH;
+    if (hipEventCreateWithFlags(&after, hipEventDisableTiming) != hipSuccess) {
+      hipEventDestroy(before);
+      return QOPT_ELAUNCH;
+    }
+    if (hipEventRecord(before, stream) != hipSuccess ||
+        hipStreamWaitEvent(second, before, 0) != hipSuccess) {
+      hipEventDestroy(before);
+      hipEventDestroy(after);
+      return QOPT_ELAUNCH;
+    }
+  }
+  uint64_t index = 0;
   bool fits = true;
-  return plan_chunks<Chunk>(
+  rc = plan_chunks<Chunk>(
       ntensors, size_of, fill, nchunks, total,
       [&](const Chunk& c, uint64_t blocks) {
         unsigned grid = 0;
         int r = grid_for(kernel, static_cast<uint32_t>(blocks), cap, run, &grid);
         if (r != QOPT_OK) return r;
-        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, c, args...);
+        hipStream_t s = (index++ & 1) ? second : stream;
+        hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, c, args...);
         return launch_status();
       },
       &fits);
+  if (fork) {
+    // join whatever was enqueued, also after a failed launch
+    if (hipEventRecord(after, second) != hipSuccess ||
+        hipStreamWaitEvent(stream, after, 0) != hipSuccess)
+      rc = QOPT_ELAUNCH;
+    hipEventDestroy(before);
+    hipEventDestroy(after);
+  }
+  return rc;
 }
 
 // Descriptor fillers of the step and the codec.
@@ -1305,9 +1363,9 @@ template <typename PT, typename GT, int kMode>
 int launch_step_mode(const qopt_tensor* tensors, int32_t ntensors, size_t psize, size_t gsize,
                      const AdamScalars& k, const qopt_codebook* cbm, const qopt_codebook* cbv,
                      hipStream_t stream) {
-  return launch_planned<StepChunk>(adam8bit_kernel<PT, GT, kMode>, 0, step_run<PT, GT>(), ntensors,
-                                   StepSize{tensors}, StepFill{tensors, psize, gsize}, stream, k,
-                                   cbm, cbv);
+  return launch_planned<StepChunk, std::is_same<PT, uint16_t>::value>(
+      adam8bit_kernel<PT, GT, kMode>, 0, step_run<PT, GT>(), ntensors, StepSize{tensors},
+      StepFill{tensors, psize, gsize}, stream, k, cbm, cbv);
 }
 
 // mode: a ScreenMode, which only bf16 parameters use.
@@ -1513,8 +1571,9 @@ int launch_traffic_probe(const qopt_tensor* tensors, int32_t ntensors, size_t ps
   int per_cu = 0;
   const int rc = step_wg_per_cu<PT, GT>(&per_cu);
   if (rc != QOPT_OK) return rc;
-  return launch_planned<StepChunk>(step_traffic_kernel<PT, GT>, per_cu, step_run<PT, GT>(), ntensors,
-                                   StepSize{tensors}, StepFill{tensors, psize, gsize}, stream);
+  return launch_planned<StepChunk, std::is_same<PT, uint16_t>::value>(
+      step_traffic_kernel<PT, GT>, per_cu, step_run<PT, GT>(), ntensors, StepSize{tensors},
+      StepFill{tensors, psize, gsize}, stream);
 }
 
 extern "C" int qopt_adam8bit_traffic_probe(const qopt_tensor* tensors, int32_t ntensors,

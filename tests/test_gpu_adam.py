@@ -794,6 +794,70 @@ def sampled_trajectory(q, shapes, pdt, gdt, steps, seed, grad_fill, tmp_path, sa
     assert_params(gp, ref["p"], pdt, HP["lr"], f"({sample.size} sampled blocks)")
 
 
+def test_bf16_steps_from_two_threads_on_two_streams(q, tmp_path):
+    """bf16 parameters spread a step's launches over the caller's stream and a second
+    stream of the library's: two host threads, each stepping its own tensor of
+    2^18 + 3000 blocks (two launches) on its own stream, twice, while the other does
+    the same.  Sampled blocks (both sides of the launch split among them) must match
+    the oracle."""
+    import threading
+    nblk = (1 << 18) + 3000
+    n = nblk * BLOCK
+    sets = {}
+    for k, seed in (("a", 11), ("b", 12)):
+        P = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+        workloads.fill_normal_(P, 0.02, seed)
+        G = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+        for i, g in enumerate(G):
+            workloads.fill_normal_(g, 1e-3, seed * 10 + i)
+        st = dev_state(n)
+        sets[k] = (P, G, st)
+    nlaunch = q.qopt_adam8bit_launch_count([(sets["a"][0], sets["a"][1][0], *sets["a"][2])])
+    assert nlaunch == 2
+    half = -(-nblk // 2)
+    sample = workloads.sample_blocks(nblk, 300, 5, must=[half - 1, half])
+    sidx = torch.from_numpy(sample).cuda()
+
+    def gather(flat, dtype):
+        return to_host(flat.view(-1, BLOCK)[sidx].reshape(-1), dtype)
+
+    inputs = {k: {"p0": gather(P, "bf16"), "g1": gather(G[0], "bf16"), "g2": gather(G[1], "bf16")}
+              for k, (P, G, st) in sets.items()}
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(k):
+        try:
+            P, G, st = sets[k]
+            stream = torch.cuda.Stream()
+            with torch.cuda.stream(stream):
+                for step in (1, 2):
+                    q.qopt_adam8bit_step([(P, G[step - 1], *st)], step=step, **HP)
+            stream.synchronize()
+        except Exception as e:  # reported below, in the main thread
+            errors.append(e)
+
+    say(f"two threads, bf16 params, {nblk} blocks each, {nlaunch} launches per step")
+    threads = [threading.Thread(target=run, args=(k,)) for k in sets]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    cfg = dict(HP, steps=2, pdt="bf16", gdt="bf16")
+    for k, (P, G, st) in sets.items():
+        got = [gather(st[0], "u8"), gather(st[1], "u8"), st[2][sidx].cpu().numpy(), st[3][sidx].cpu().numpy()]
+        gp = gather(P, "bf16")
+        sub = tmp_path / k
+        sub.mkdir()
+        ref = run_oracle_blocks(inputs[k], cfg, sample.size, str(sub))
+        what = f"(set {k}, {sample.size} sampled blocks)"
+        assert_state(got, [ref["cm"], ref["cv"], ref["am"], ref["av"]], what)
+        assert_params(gp, ref["p"], "bf16", HP["lr"], what)
+    del sets
+    torch.cuda.empty_cache()
+
+
 def _dense_grads(std, seed, outlier_frac=0.0, outlier_scale=1.0):
     def fill(G, step):
         workloads.fill_normal_(G, std, seed * 1000 + step)
