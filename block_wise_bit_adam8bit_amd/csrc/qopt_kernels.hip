@@ -1267,9 +1267,9 @@ int count_chunks(int32_t ntensors, const SizeOf& size_of, const Fill& fill,
 // ones; the second stream starts after the work queued on `stream` before the call,
 // and `stream` waits for the second stream's launches before anything queued after
 // the call.  The launches touch disjoint blocks, so their order does not matter.
-// Measured in one process on the same buffers: the 20B bf16 step (38 launches) 4.9 %
-// faster in two processes; the fp32-parameter steps 1-1.6 % slower, so they keep one
-// stream.
+// Measured in one process on the same buffers: the 20B bf16 step (38 launches)
+// 4.8-5.8 % faster (three processes); the fp32-parameter steps 1-1.6 % slower, so they
+// keep one stream.
 template <typename Chunk, bool kFork = false, typename Kernel, typename SizeOf, typename Fill,
           typename... Args>
 int launch_planned(Kernel kernel, int cap, uint32_t run, int32_t ntensors, const SizeOf& size_of,

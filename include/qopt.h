@@ -26,7 +26,9 @@
  *     different streams are independent.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Device work is
  *     enqueued on it and the call returns without synchronising; errors raised by
- *     the device surface when the caller synchronises.
+ *     the device surface when the caller synchronises.  (The bf16-parameter step
+ *     and its traffic probe also use one stream of the library's per device, joined
+ *     back into `stream`: see qopt_adam8bit_step.)
  *   - Arguments are checked on the host before anything is enqueued; a failed check
  *     returns an error code and enqueues nothing.  n == 0 is a no-op returning
  *     QOPT_OK.  No C++ exception crosses this interface.
@@ -215,7 +217,12 @@ typedef struct qopt_adam_hparams {
  * Checks: tensors != NULL when ntensors > 0, ntensors >= 0, every n >= 0, non-null
  * pointers for n > 0, lr and eps finite, eps >= 0, 0 <= beta < 1, step >= 1.
  * Tensors with n == 0 are skipped.  Large tensor lists are split into several
- * launches on `stream` of equal block counts (qopt_adam8bit_launch_count).
+ * launches of equal block counts (qopt_adam8bit_launch_count), on `stream`; with bf16
+ * parameters and more than one launch, every other launch goes on a second stream
+ * that the library creates once per device (non-blocking, default priority, kept
+ * until the process ends).  That stream first waits for the work enqueued on `stream`
+ * before the call, and `stream` waits for its launches before any work enqueued after
+ * the call, so the call orders on `stream` as one unit.
  */
 int qopt_adam8bit_step(const qopt_tensor* tensors, int32_t ntensors, int param_dtype,
                        int grad_dtype, const qopt_codebook* cb_m_dev,
@@ -241,7 +248,8 @@ int qopt_adam8bit_launch_count(const qopt_tensor* tensors, int32_t ntensors, int
  * same buffers gives the ceiling of the step's access pattern.  Only blocks on the
  * step's vector path (full blocks of tensors whose pointers allow vector accesses)
  * are moved.  Same argument checks as qopt_adam8bit_step (no codebooks or
- * hyper-parameters); enqueued on `stream`.
+ * hyper-parameters); enqueued on `stream` (and, with bf16 parameters, over the second
+ * stream as the step's launches are).
  */
 int qopt_adam8bit_traffic_probe(const qopt_tensor* tensors, int32_t ntensors, int param_dtype,
                                 int grad_dtype, void* stream);

@@ -609,6 +609,47 @@ def test_step_runs_on_the_callers_stream(q):
         assert_params(to_host(dp[i], pdt), out[0], pdt, HP["lr"], what)
 
 
+def test_bf16_step_runs_on_the_callers_stream(q, tmp_path):
+    """bf16 parameters with two launches (2^18 + 3000 blocks), which the step spreads
+    over the caller's stream and a second stream of the library's: on a side stream
+    queued behind long matrix products and the copy that fills the gradients, both
+    launches must see those gradients (the second stream waits for the caller's), and
+    sampled blocks on both sides of the launch split must match the oracle."""
+    nblk = (1 << 18) + 3000
+    n = nblk * BLOCK
+    P = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    workloads.fill_normal_(P, 0.02, 21)
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    workloads.fill_normal_(src, 1e-3, 22)
+    G = torch.zeros_like(src)
+    st = dev_state(n)
+    assert q.qopt_adam8bit_launch_count([(P, G, *st)]) == 2
+    half = -(-nblk // 2)
+    sample = workloads.sample_blocks(nblk, 300, 23, must=[half - 1, half])
+    sidx = torch.from_numpy(sample).cuda()
+
+    def gather(flat, dtype):
+        return to_host(flat.view(-1, BLOCK)[sidx].reshape(-1), dtype)
+
+    inputs = {"p0": gather(P, "bf16"), "g1": gather(src, "bf16")}
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    say(f"side stream bf16 step, {nblk} blocks")
+    _busy(side)
+    with torch.cuda.stream(side):
+        G.copy_(src)
+        q.qopt_adam8bit_step([(P, G, *st)], step=1, **HP)
+    side.synchronize()
+    got = [gather(st[0], "u8"), gather(st[1], "u8"), st[2][sidx].cpu().numpy(), st[3][sidx].cpu().numpy()]
+    gp = gather(P, "bf16")
+    ref = run_oracle_blocks(inputs, dict(HP, steps=1, pdt="bf16", gdt="bf16"), sample.size, str(tmp_path))
+    what = f"({sample.size} sampled blocks, side stream)"
+    assert_state(got, [ref["cm"], ref["cv"], ref["am"], ref["av"]], what)
+    assert_params(gp, ref["p"], "bf16", HP["lr"], what)
+    del P, src, G, st
+    torch.cuda.empty_cache()
+
+
 def test_steps_from_two_threads_on_two_streams(q):
     """Two host threads step two disjoint tensor sets at once, each on its own stream
     (default priority): the library keeps no per-call state, so both match the oracle."""
