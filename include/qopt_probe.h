@@ -7,9 +7,11 @@
  * parameters, 4 KB of gradients and 2 KB of each code stream, and writes the
  * parameters and both code streams back (the block maxima are left out: 16 bytes per
  * block).  What it writes is what it read, so every buffer keeps its contents.  The
- * patterns differ only in how waves walk the blocks and order their accesses; timed
- * against the step on the same buffers they map the ceiling of this 57 % read /
- * 43 % write mix on the device (see the ceiling study of bench.py).
+ * patterns differ only in how waves walk the blocks and order their accesses, and in
+ * when they issue them: the paced patterns issue every wave's reads and writes at the
+ * start of each period of the chip's real-time counter.  Timed against the step on
+ * the same buffers they map the ceiling of this 57 % read / 43 % write mix on the
+ * device (see the ceiling study of bench.py).
  */
 #ifndef QOPT_PROBE_H
 #define QOPT_PROBE_H
@@ -28,7 +30,8 @@ int qopt_pattern_probe_count(void);
 /*
  * A static description of pattern `pattern` (NULL outside the range): its lookahead
  * (blocks whose loads are in flight per wave), blocks walked consecutively per wave,
- * waves per SIMD, access width of the code streams and order of a block's accesses.
+ * waves per SIMD, access width of the code streams, order of a block's accesses and,
+ * for a paced pattern, the rate its period is sized for.
  */
 const char* qopt_pattern_probe_name(int pattern);
 
