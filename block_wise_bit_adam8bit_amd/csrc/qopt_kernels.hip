@@ -388,6 +388,9 @@ quantize_kernel(CodecChunk c, const qopt_codebook* cb_g) {
     if (b < piece.begin || b >= piece.end) piece = find_piece(c, b);
     return block_of(piece, b);
   };
+  // A and B take turns: a block is encoded from one set while the other set's loads
+  // and the loads issued right after its own encoding (the block two strides on) are
+  // in flight.  Launches hold at most 2^18 blocks, so the indices cannot wrap.
   f32x4 A[kSlices], B[kSlices];
   CodecRef ra = ref_at(blk);
   if (ra.vec) load_vec(ra, A);
